@@ -1,0 +1,260 @@
+/*
+ * oxa.h - BF16 attention over a paged KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  Four operations make up the path:
+ *
+ *   oxa_paged_append_rope  fused NeoX RoPE on q/k + append of (k, v) into
+ *                          exclusively owned KV pages
+ *   oxa_paged_decode       paged batch decode (MHA / GQA / MQA), optionally
+ *                          split-K over explicit KV partitions with an f32
+ *                          partial workspace and a log-sum-exp merge
+ *   oxa_ragged_prefill     causal (or full) prefill over packed ragged K/V
+ *   oxa_paged_prefill      causal (or full) prefill over paged K/V
+ *
+ * The operator contracts follow the "FlashInfer parity matrix" page (sections
+ * "Admitted attention matrix", "Dispatch limits", "Paged KV ownership
+ * difference", "Domain coverage") and the runtime rules on the "Oxide Infer"
+ * README page (sections "One execution model" and "Providers": caller-selected
+ * stream, typed read and write regions, checked span / alignment / alias /
+ * capacity, explicit workspace, typed device-status failures, no tuning or
+ * silent fallback at enqueue).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Types.   bf16 tensors are passed as uint16_t bit patterns; indices are int32.
+ * Memory.  Every tensor pointer is a DEVICE pointer (hipMalloc'd or a torch
+ *          CUDA tensor), except where a comment says "host".  The caller owns
+ *          all memory.  The library allocates nothing, frees nothing, keeps no
+ *          pointer after the call returns and has no global mutable state.
+ * Stream.  Work is enqueued on `stream` (0 = the null stream) and the call
+ *          returns without synchronising.  Buffers must stay valid, and inputs
+ *          unmodified, until that work completes.
+ * Errors.  Host-detectable contract violations (null pointer, unsupported
+ *          shape, misalignment, overlapping regions, short workspace) return
+ *          an OXA_ERR_* code at once and enqueue NOTHING.  Data-dependent
+ *          violations (bad indptr, page ids outside the pool, lengths beyond
+ *          the declared maxima, refcount != 1, positions beyond capacity) are
+ *          reported through the `status` array on the stream; kernels never
+ *          read or write outside the regions the arguments describe, whatever
+ *          the metadata holds.  Rows of a sequence whose status is non-zero
+ *          are unspecified.
+ * Domain.  head_dim must be 128 and page_size 16 (OXA_ERR_UNSUPPORTED else).
+ *          Head grouping: num_qo_heads % num_kv_heads == 0; q head h reads
+ *          kv head h / (num_qo_heads / num_kv_heads).
+ * Layouts. K and V live in two pools of num_pages pages each:
+ *            OXA_LAYOUT_NHD: [num_pages][page_size][num_kv_heads][head_dim]
+ *            OXA_LAYOUT_HND: [num_pages][num_kv_heads][page_size][head_dim]
+ * Pages.   Sequence b lists its physical pages in
+ *          page_indices[page_indptr[b] .. page_indptr[b+1]); its logical token
+ *          j is slot j % 16 of page page_indices[page_indptr[b] + j / 16].
+ *          Pages may appear in any physical order, and attention may read a
+ *          page listed by several sequences.  A sequence may list more pages
+ *          than its length needs; attention reads only the first
+ *          ceil(len / 16).  num_page_entries is the length of page_indices.
+ * Alignment. Every bf16 tensor and the workspace must be 16-byte aligned.
+ * Softmax. f32 running max / sum / accumulator; outputs rounded to bf16
+ *          (nearest-even).  lse (optional, may be NULL) is the natural-log
+ *          log-sum-exp of the scaled scores of each (query row, q head).
+ */
+#ifndef OXA_H
+#define OXA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OXA_ABI_VERSION 1
+#define OXA_PAGE_SIZE 16
+#define OXA_HEAD_DIM 128
+
+typedef enum { OXA_LAYOUT_NHD = 0, OXA_LAYOUT_HND = 1 } oxa_layout;
+
+typedef enum {
+  OXA_OK = 0,
+  /* returned by the call itself; nothing was enqueued */
+  OXA_ERR_NULL = 1,          /* a required pointer is NULL */
+  OXA_ERR_UNSUPPORTED = 2,   /* head_dim != 128, page_size != 16, unknown layout */
+  OXA_ERR_SHAPE = 3,         /* a count is out of range, or Hq % Hkv != 0 */
+  OXA_ERR_ALIGN = 4,         /* a bf16 tensor or the workspace is not 16-byte aligned */
+  OXA_ERR_ALIAS = 5,         /* an output region overlaps an input or another output */
+  OXA_ERR_WORKSPACE = 6,     /* workspace NULL or smaller than the size query returns */
+  OXA_ERR_LAUNCH = 7,        /* the HIP runtime refused a kernel launch */
+  /* written to status[] on the stream by the kernels */
+  OXA_DEV_PAGE_RANGE = 16,   /* a needed page id is outside [0, num_pages) */
+  OXA_DEV_INDPTR = 17,       /* indptr out of order / beyond its array, or too few pages */
+  OXA_DEV_SEQ_LEN = 18,      /* a length is < 1 (where required) or above its declared max */
+  OXA_DEV_CAUSAL = 19,       /* causal with more query rows than keys */
+  OXA_DEV_NOT_EXCLUSIVE = 20,/* an append target page has refcount != 1 */
+  OXA_DEV_CAPACITY = 21,     /* an append position is < 0 or beyond the listed pages */
+  OXA_DEV_BATCH_INDEX = 22   /* an append token names a sequence outside [0, batch) */
+} oxa_status;
+
+/* ABI version compiled into the library (OXA_ABI_VERSION). */
+int32_t oxa_abi_version(void);
+
+/* Static, human-readable name of a status code ("OXA_OK", ...; "unknown"). */
+const char* oxa_status_string(int32_t code);
+
+/*
+ * Fused NeoX RoPE + paged KV append into exclusively owned pages.
+ * ("FlashInfer parity matrix": rows Standard RoPE and Fused RoPE plus paged
+ * append; section "Paged KV ownership difference": append accepts an
+ * authoritative per-page reference-count snapshot and writes only pages whose
+ * count is one.  "Oxide Infer" README, "Operator surface": BF16 NeoX RoPE with
+ * explicit positions.)
+ *
+ * For every token t (0 <= t < nnz) of sequence b = batch_indices[t] at
+ * position p = positions[t] (one int32 serves as the RoPE position and the
+ * token's logical KV slot):
+ *   - k_rot = RoPE(k_in[t], p), v = v_in[t]   ([num_kv_heads][128] each)
+ *   - both are stored at slot p % 16 of page page_indices[page_indptr[b] + p/16]
+ *   - if q_in != NULL: q_out[t] = RoPE(q_in[t], p)   ([num_qo_heads][128])
+ * RoPE: pair (i, i + 64), angle a = p * rope_theta^(-2i/128) (evaluated in
+ * double precision), (x_i cos a - x_{i+64} sin a, x_{i+64} cos a + x_i sin a),
+ * rounded once to bf16.
+ *
+ * All or nothing: a first kernel checks every token (batch index in
+ * [0, batch), position in [0, 16 * pages listed for b), page id in
+ * [0, num_pages), page_refcounts[page] == 1) and writes status[0] = 0 or the
+ * OXA_DEV_* code of the lowest failing token, status[1] = that token or -1.
+ * The writing kernel runs only if status[0] == 0; otherwise no pool byte and
+ * no q_out byte changes.  Two tokens naming the same (page, slot) break the
+ * contract (the result is unspecified).
+ *
+ * Shapes: q_in/q_out [nnz][num_qo_heads][128]; k_in/v_in [nnz][num_kv_heads][128];
+ * batch_indices/positions [nnz]; page_indptr [batch+1];
+ * page_indices [num_page_entries]; page_refcounts [num_pages]; status [2].
+ * q_out may equal q_in (in place) but may not overlap it otherwise; q_in and
+ * q_out are both NULL or both non-NULL (num_qo_heads is then ignored).
+ * Ranges: 0 <= nnz (0 = no-op apart from status), 1 <= batch.
+ */
+oxa_status oxa_paged_append_rope(
+    hipStream_t stream,
+    const uint16_t* q_in, uint16_t* q_out, int32_t num_qo_heads,
+    const uint16_t* k_in, const uint16_t* v_in, int32_t num_kv_heads, int32_t head_dim,
+    const int32_t* batch_indices, const int32_t* positions, int32_t nnz,
+    uint16_t* k_pages, uint16_t* v_pages, int32_t num_pages, int32_t page_size, int32_t layout,
+    const int32_t* page_indptr, int32_t batch,
+    const int32_t* page_indices, int32_t num_page_entries,
+    const int32_t* page_refcounts, float rope_theta,
+    int32_t* status);
+
+/*
+ * Paged batch decode: one query token per sequence over its paged KV.
+ * ("FlashInfer parity matrix", Admitted attention matrix: Paged batch decode
+ * - MHA, MQA, GQA, mixed lengths, page order, read-only page reuse; Single
+ * decode split-K - explicit partitions, F32 partial workspace and a merge.)
+ *
+ * o[b][h] = sum_j softmax_j(sm_scale * <q[b][h], k_j>) v_j over the
+ * seq_lens[b] tokens of sequence b, kv head h / (Hq / Hkv).
+ *
+ * num_partitions P >= 1 splits each sequence into explicit partitions of
+ * C = ceil(ceil(max_seq_len / 16) / P) pages: partition p holds the tokens
+ * [16*C*p, min(16*C*(p+1), seq_len)).  With P == 1 one kernel writes o (and
+ * lse) directly and no workspace is needed.  With P > 1 the partial states go
+ * to the workspace and a merge kernel combines them; the workspace then holds,
+ * on completion,
+ *     o_part   f32 [batch][num_qo_heads][P][128]  normalised partial outputs
+ *     lse_part f32 [batch][num_qo_heads][P]       natural-log partial lse
+ *                                                  (-inf for an empty partition,
+ *                                                  whose o_part row is 0)
+ * laid out back to back from the workspace pointer (o_part first).
+ *
+ * status (may be NULL) [batch]: status[b] = 0 or the first failing check of
+ * sequence b in the order OXA_DEV_SEQ_LEN (1 <= seq_len <= max_seq_len),
+ * OXA_DEV_INDPTR (0 <= page_indptr[b] <= page_indptr[b+1] <= num_page_entries
+ * and 16 * pages >= seq_len), OXA_DEV_PAGE_RANGE (a needed page id outside
+ * [0, num_pages)).  Every status word is written on every call.
+ *
+ * Shapes: q, o [batch][num_qo_heads][128]; lse [batch][num_qo_heads] or NULL;
+ * page_indptr [batch+1]; seq_lens [batch].  Ranges: 1 <= batch,
+ * 1 <= max_seq_len, 1 <= num_partitions <= 1024.
+ */
+oxa_status oxa_paged_decode(
+    hipStream_t stream,
+    const uint16_t* q, int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+    const uint16_t* k_pages, const uint16_t* v_pages, int32_t num_pages, int32_t page_size,
+    int32_t layout,
+    const int32_t* page_indptr, const int32_t* page_indices, int32_t num_page_entries,
+    const int32_t* seq_lens, int32_t max_seq_len,
+    float sm_scale, int32_t num_partitions,
+    void* workspace, size_t workspace_bytes,
+    uint16_t* o, float* lse, int32_t* status);
+
+/* Workspace bytes oxa_paged_decode needs (0 for num_partitions == 1). */
+size_t oxa_paged_decode_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t head_dim,
+                                        int32_t num_partitions);
+
+/*
+ * Ragged prefill: sequence b's query rows q[qo_indptr[b] .. qo_indptr[b+1])
+ * attend to k/v[kv_indptr[b] .. kv_indptr[b+1]).  ("FlashInfer parity
+ * matrix", Admitted attention matrix: Ragged causal prefill.)
+ *
+ * causal != 0 masks bottom-right: query row i of a sequence with qo_len rows
+ * and kv_len keys sees keys j <= i + (kv_len - qo_len).  causal == 0 lets every
+ * row see every key.
+ *
+ * status (may be NULL) [batch]: 0 or the first failing check of sequence b:
+ * OXA_DEV_INDPTR (each indptr non-decreasing from >= 0 and within nnz),
+ * OXA_DEV_SEQ_LEN (qo_len <= max_qo_len, kv_len <= max_kv_len, kv_len >= 1
+ * when qo_len >= 1), OXA_DEV_CAUSAL (causal and qo_len > kv_len).
+ *
+ * Shapes: q, o [nnz_qo][num_qo_heads][128]; k, v [nnz_kv][num_kv_heads][128];
+ * lse [nnz_qo][num_qo_heads] or NULL; qo_indptr, kv_indptr [batch+1].
+ * The workspace is reserved (the size query returns 0; pass NULL, 0).
+ * Ranges: 1 <= batch, 0 <= nnz_qo, nnz_kv; 1 <= max_qo_len, max_kv_len.
+ */
+oxa_status oxa_ragged_prefill(
+    hipStream_t stream,
+    const uint16_t* q, const uint16_t* k, const uint16_t* v,
+    const int32_t* qo_indptr, const int32_t* kv_indptr,
+    int32_t batch, int32_t nnz_qo, int32_t nnz_kv,
+    int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t max_qo_len, int32_t max_kv_len, int32_t causal, float sm_scale,
+    void* workspace, size_t workspace_bytes,
+    uint16_t* o, float* lse, int32_t* status);
+
+size_t oxa_ragged_prefill_workspace_bytes(int32_t batch, int32_t nnz_qo, int32_t num_qo_heads,
+                                          int32_t head_dim);
+
+/*
+ * Paged prefill: sequence b's query rows q[qo_indptr[b] .. qo_indptr[b+1])
+ * attend to the first seq_lens[b] tokens of its paged KV.  ("FlashInfer
+ * parity matrix", Admitted attention matrix: Paged causal prefill; Graph
+ * evidence: invalid-page rejection.)  Causal alignment as in
+ * oxa_ragged_prefill with kv_len = seq_lens[b].
+ *
+ * status (may be NULL) [batch]: 0 or the first failing check of sequence b:
+ * OXA_DEV_INDPTR (qo_indptr / page_indptr ranges), OXA_DEV_SEQ_LEN
+ * (qo_len <= max_qo_len, 0 <= seq_len <= max_seq_len, seq_len >= 1 when
+ * qo_len >= 1), OXA_DEV_INDPTR (too few pages for seq_len), OXA_DEV_CAUSAL,
+ * OXA_DEV_PAGE_RANGE.
+ *
+ * Shapes: q, o [nnz_qo][num_qo_heads][128]; lse [nnz_qo][num_qo_heads] or
+ * NULL; qo_indptr, page_indptr [batch+1]; seq_lens [batch].
+ * The workspace is reserved (the size query returns 0; pass NULL, 0).
+ */
+oxa_status oxa_paged_prefill(
+    hipStream_t stream,
+    const uint16_t* q, const int32_t* qo_indptr,
+    const uint16_t* k_pages, const uint16_t* v_pages, int32_t num_pages, int32_t page_size,
+    int32_t layout,
+    const int32_t* page_indptr, const int32_t* page_indices, int32_t num_page_entries,
+    const int32_t* seq_lens,
+    int32_t batch, int32_t nnz_qo, int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t max_qo_len, int32_t max_seq_len, int32_t causal, float sm_scale,
+    void* workspace, size_t workspace_bytes,
+    uint16_t* o, float* lse, int32_t* status);
+
+size_t oxa_paged_prefill_workspace_bytes(int32_t batch, int32_t nnz_qo, int32_t num_qo_heads,
+                                         int32_t head_dim);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OXA_H */

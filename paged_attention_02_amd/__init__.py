@@ -1,0 +1,216 @@
+"""Python binding of liboxa: BF16 attention over a paged KV cache on MI355X (gfx950).
+
+The functions below carry the names of the C ABI declared in ``include/oxa.h``
+and do argument marshalling only: they take torch tensors that live on the GPU
+(bf16 tensors as ``torch.bfloat16`` or ``torch.int16``/``uint16`` views,
+indices as ``torch.int32``), pass their device pointers and the current HIP
+stream to the library and return its status code.  Every step of the
+computation runs in the library's kernels; if the library cannot be loaded the
+call raises.
+
+Status codes: ``OXA_OK`` (0); host-detected errors ``OXA_ERR_*`` (returned at
+once, nothing enqueued); device-detected ``OXA_DEV_*`` codes land in the
+``status`` tensor after the stream completes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboxa.so")
+
+OXA_OK = 0
+OXA_ERR_NULL = 1
+OXA_ERR_UNSUPPORTED = 2
+OXA_ERR_SHAPE = 3
+OXA_ERR_ALIGN = 4
+OXA_ERR_ALIAS = 5
+OXA_ERR_WORKSPACE = 6
+OXA_ERR_LAUNCH = 7
+OXA_DEV_PAGE_RANGE = 16
+OXA_DEV_INDPTR = 17
+OXA_DEV_SEQ_LEN = 18
+OXA_DEV_CAUSAL = 19
+OXA_DEV_NOT_EXCLUSIVE = 20
+OXA_DEV_CAPACITY = 21
+OXA_DEV_BATCH_INDEX = 22
+
+LAYOUTS = {"NHD": 0, "HND": 1}
+PAGE_SIZE = 16
+HEAD_DIM = 128
+
+# C signatures: (name, restype, argtypes)
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_F = ctypes.c_float
+_Z = ctypes.c_size_t
+SIGNATURES = {
+    "oxa_abi_version": (_I, []),
+    "oxa_status_string": (ctypes.c_char_p, [_I]),
+    "oxa_paged_append_rope": (_I, [_P, _P, _P, _I, _P, _P, _I, _I, _P, _P, _I, _P, _P, _I, _I, _I,
+                                   _P, _I, _P, _I, _P, _F, _P]),
+    "oxa_paged_decode": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _P, _P, _I, _P, _I, _F,
+                              _I, _P, _Z, _P, _P, _P]),
+    "oxa_paged_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
+    "oxa_ragged_prefill": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
+                                _P, _Z, _P, _P, _P]),
+    "oxa_ragged_prefill_workspace_bytes": (_Z, [_I, _I, _I, _I]),
+    "oxa_paged_prefill": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _I, _P, _I, _I, _I, _I, _I,
+                               _I, _I, _I, _F, _P, _Z, _P, _P, _P]),
+    "oxa_paged_prefill_workspace_bytes": (_Z, [_I, _I, _I, _I]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded liboxa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"liboxa.so not found at {LIB_PATH}; build it with "
+                "`python -m paged_attention_02_amd.build` (hipcc, gfx950)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().oxa_status_string(int(code)).decode()
+
+
+class OxaError(RuntimeError):
+    def __init__(self, code: int):
+        super().__init__(f"{status_string(code)} ({code})")
+        self.code = code
+
+
+def check(code: int) -> None:
+    if code != OXA_OK:
+        raise OxaError(code)
+
+
+# ------------------------------------------------------------------ marshalling
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _bf16(t, name):
+    import torch
+    if t is not None and t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must be bf16 (or its 16-bit bit pattern)")
+    return _ptr(t)
+
+
+def _i32(t, name):
+    import torch
+    if t is not None and t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    return _ptr(t)
+
+
+def _f32(t, name):
+    import torch
+    if t is not None and t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    return _ptr(t)
+
+
+def _stream(stream) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _layout(layout) -> int:
+    return LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+
+
+# ------------------------------------------------------------------ entry points
+
+def oxa_paged_append_rope(q_in, q_out, k_in, v_in, batch_indices, positions, k_pages, v_pages,
+                          page_indptr, page_indices, page_refcounts, status, *, layout="NHD",
+                          rope_theta=10000.0, stream=None) -> int:
+    """Fused NeoX RoPE on q/k and append of (rotated k, v) into exclusive pages.
+
+    q_in/q_out [nnz, Hq, 128] (both None to skip q), k_in/v_in [nnz, Hkv, 128],
+    pools in ``layout``, status int32 [2] (code, first failing token).
+    """
+    lay = _layout(layout)
+    hkv = k_in.shape[1]
+    num_pages = k_pages.shape[0]
+    hq = q_in.shape[1] if q_in is not None else 0
+    return lib().oxa_paged_append_rope(
+        _stream(stream), _bf16(q_in, "q_in"), _bf16(q_out, "q_out"), hq, _bf16(k_in, "k_in"),
+        _bf16(v_in, "v_in"), hkv, k_in.shape[2], _i32(batch_indices, "batch_indices"),
+        _i32(positions, "positions"), k_in.shape[0], _bf16(k_pages, "k_pages"),
+        _bf16(v_pages, "v_pages"), num_pages, PAGE_SIZE, lay, _i32(page_indptr, "page_indptr"),
+        page_indptr.shape[0] - 1, _i32(page_indices, "page_indices"), page_indices.shape[0],
+        _i32(page_refcounts, "page_refcounts"), float(rope_theta), _i32(status, "status"))
+
+
+def oxa_paged_decode_workspace_bytes(batch, num_qo_heads, num_partitions, head_dim=HEAD_DIM) -> int:
+    return int(lib().oxa_paged_decode_workspace_bytes(batch, num_qo_heads, head_dim,
+                                                      num_partitions))
+
+
+def oxa_paged_decode(q, k_pages, v_pages, page_indptr, page_indices, seq_lens, o, *,
+                     max_seq_len, sm_scale, layout="NHD", num_kv_heads=None, num_partitions=1,
+                     workspace=None, lse=None, status=None, stream=None) -> int:
+    """Paged batch decode: q/o [B, Hq, 128]; lse [B, Hq] f32; status [B] int32."""
+    lay = _layout(layout)
+    if num_kv_heads is None:
+        num_kv_heads = k_pages.shape[2] if lay == 0 else k_pages.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return lib().oxa_paged_decode(
+        _stream(stream), _bf16(q, "q"), q.shape[0], q.shape[1], num_kv_heads, q.shape[2],
+        _bf16(k_pages, "k_pages"), _bf16(v_pages, "v_pages"), k_pages.shape[0], PAGE_SIZE, lay,
+        _i32(page_indptr, "page_indptr"), _i32(page_indices, "page_indices"),
+        page_indices.shape[0], _i32(seq_lens, "seq_lens"), int(max_seq_len), float(sm_scale),
+        int(num_partitions), _ptr(workspace), ws_bytes, _bf16(o, "o"), _f32(lse, "lse"),
+        _i32(status, "status"))
+
+
+def oxa_ragged_prefill(q, k, v, qo_indptr, kv_indptr, o, *, max_qo_len, max_kv_len, sm_scale,
+                       causal=True, lse=None, status=None, stream=None) -> int:
+    """Ragged prefill: q/o [nnz_qo, Hq, 128]; k/v [nnz_kv, Hkv, 128]."""
+    return lib().oxa_ragged_prefill(
+        _stream(stream), _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"),
+        _i32(qo_indptr, "qo_indptr"), _i32(kv_indptr, "kv_indptr"), qo_indptr.shape[0] - 1,
+        q.shape[0], k.shape[0], q.shape[1], k.shape[1], q.shape[2], int(max_qo_len),
+        int(max_kv_len), int(bool(causal)), float(sm_scale), None, 0, _bf16(o, "o"),
+        _f32(lse, "lse"), _i32(status, "status"))
+
+
+def oxa_paged_prefill(q, qo_indptr, k_pages, v_pages, page_indptr, page_indices, seq_lens, o, *,
+                      max_qo_len, max_seq_len, sm_scale, layout="NHD", num_kv_heads=None,
+                      causal=True, lse=None, status=None, stream=None) -> int:
+    """Paged prefill: q/o [nnz_qo, Hq, 128] over the paged K/V of each sequence."""
+    lay = _layout(layout)
+    if num_kv_heads is None:
+        num_kv_heads = k_pages.shape[2] if lay == 0 else k_pages.shape[1]
+    return lib().oxa_paged_prefill(
+        _stream(stream), _bf16(q, "q"), _i32(qo_indptr, "qo_indptr"), _bf16(k_pages, "k_pages"),
+        _bf16(v_pages, "v_pages"), k_pages.shape[0], PAGE_SIZE, lay,
+        _i32(page_indptr, "page_indptr"), _i32(page_indices, "page_indices"),
+        page_indices.shape[0], _i32(seq_lens, "seq_lens"), qo_indptr.shape[0] - 1, q.shape[0],
+        q.shape[1], num_kv_heads, q.shape[2], int(max_qo_len), int(max_seq_len),
+        int(bool(causal)), float(sm_scale), None, 0, _bf16(o, "o"), _f32(lse, "lse"),
+        _i32(status, "status"))

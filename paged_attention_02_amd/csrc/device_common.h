@@ -1,0 +1,109 @@
+// Device-side helpers shared by the gfx950 kernels of liboxa.
+//
+// Matrix-core fragment layouts (gfx950, wave64), as used throughout:
+//   v_mfma_f32_32x32x16_bf16  C[32x32] += A[32x16] * B[16x32]
+//     A operand: lane l holds A[m = l%32][k = 8*(l/32) + j], j = 0..7
+//     B operand: lane l holds B[k = 8*(l/32) + j][n = l%32], j = 0..7
+//     C result : lane l, reg r holds C[m = 8*(r/4) + 4*(l/32) + r%4][n = l%32]
+// A reduction over k does not depend on which physical k a lane slot stands
+// for, as long as A and B use the same assignment; the kernels use that
+// freedom to make every lane's global or LDS read one contiguous vector.
+//
+// LDS transpose read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// output lane i, element e (of 4 bf16) is source element i%4 of the 8 bytes
+// addressed by lane 4*e + i/4 of the group.  If lanes 4e..4e+3 point at the
+// four 8-byte pieces of a 16-element row segment of "row e", lane i receives
+// column i of rows 0..3 - a 4x16 -> 16x4 transpose.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace oxa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+constexpr int kPage = 16;
+constexpr int kHeadDim = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// bf16 halves of a 32-bit word -> f32 (exact)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two f32 -> packed bf16x2 (hardware convert, round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// Round a double to bf16 (nearest, ties to even) in one step from its bits.
+// The bf16 significand keeps 8 bits; subnormal results use the fixed quantum
+// 2^-133; magnitudes that round past the largest finite bf16 become infinity.
+__host__ __device__ __forceinline__ uint16_t bf16_from_double_rne(double x) {
+  uint64_t u;
+  __builtin_memcpy(&u, &x, 8);
+  const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
+  const uint64_t a = u & 0x7fffffffffffffffull;
+  if (a >= 0x7ff0000000000000ull)
+    return (uint16_t)(a == 0x7ff0000000000000ull ? (sign | 0x7f80u) : 0x7fc0u);
+  const int e = (int)(a >> 52);
+  if (e == 0) return (uint16_t)sign;  // double zero or subnormal: far below bf16's range
+  const int eb = e - 896;             // bf16 biased exponent of the same binade
+  const uint64_t mant = (a & 0xfffffffffffffull) | 0x10000000000000ull;
+  const int shift = eb >= 1 ? 45 : 46 - eb;
+  if (shift > 54) return (uint16_t)sign;
+  uint64_t q = mant >> shift;
+  const uint64_t rem = mant & ((1ull << shift) - 1);
+  const uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (q & 1))) ++q;
+  uint32_t bits;
+  if (eb >= 1) {
+    uint32_t E = (uint32_t)eb;
+    if (q >> 8) { q >>= 1; ++E; }
+    if (E >= 255) return (uint16_t)(sign | 0x7f80u);
+    bits = (E << 7) | (uint32_t)(q & 0x7f);
+  } else {
+    bits = (uint32_t)q;  // a carry into 0x80 is the smallest normal, encoded alike
+  }
+  return (uint16_t)(sign | bits);
+}
+
+// max of v over the lane pair (l, l ^ 32)
+__device__ __forceinline__ float pair_max32(float v) {
+  const uint32_t b = __float_as_uint(v);
+  auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum32(float v) {
+  const uint32_t b = __float_as_uint(v);
+  auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ u32x4_t ldg16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// 8 bytes through the LDS transpose read; `p` is a generic pointer into LDS.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
+  i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, r);
+}
+
+}  // namespace oxa

@@ -1,0 +1,63 @@
+// Internal launch interface between the C-ABI host layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace oxa {
+
+struct DecodeLaunch {
+  const uint16_t* q;
+  const uint16_t* k_pages;
+  const uint16_t* v_pages;
+  const int32_t* page_indptr;
+  const int32_t* page_indices;
+  const int32_t* seq_lens;
+  uint16_t* o;
+  float* lse;
+  int32_t* status;
+  float* ws_o;      // [batch][hq][P][128] when num_partitions > 1
+  float* ws_lse;    // [batch][hq][P]
+  int32_t batch, hq, hkv, layout;
+  int32_t num_pages, num_page_entries, max_seq_len, num_partitions, chunk_pages;
+  float sm_scale;
+};
+hipError_t launch_paged_decode(const DecodeLaunch& a, hipStream_t stream);
+
+struct AppendLaunch {
+  const uint16_t* q_in;
+  uint16_t* q_out;
+  const uint16_t* k_in;
+  const uint16_t* v_in;
+  const int32_t* batch_indices;
+  const int32_t* positions;
+  uint16_t* k_pages;
+  uint16_t* v_pages;
+  const int32_t* page_indptr;
+  const int32_t* page_indices;
+  const int32_t* page_refcounts;
+  int32_t* status;
+  int32_t hq, hkv, nnz, num_pages, layout, batch, num_page_entries;
+  double inv_freq[64];  // rope_theta^(-2i/128), i < 64, computed on the host in double
+};
+hipError_t launch_paged_append_rope(const AppendLaunch& a, hipStream_t stream);
+
+struct PrefillLaunch {
+  const uint16_t* q;
+  const uint16_t* k;        // ragged: [nnz_kv][hkv][128]; paged: the K pool
+  const uint16_t* v;
+  const int32_t* qo_indptr;
+  const int32_t* kv_indptr;    // ragged only
+  const int32_t* page_indptr;  // paged only
+  const int32_t* page_indices;
+  const int32_t* seq_lens;
+  uint16_t* o;
+  float* lse;
+  int32_t* status;
+  int32_t paged, layout, batch, nnz_qo, nnz_kv, hq, hkv, max_qo_len, max_kv_len, causal;
+  int32_t num_pages, num_page_entries;
+  float sm_scale;
+};
+hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream);
+
+}  // namespace oxa

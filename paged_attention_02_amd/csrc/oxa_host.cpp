@@ -1,0 +1,385 @@
+// C-ABI entry points of liboxa: argument validation, workspace sizing and
+// launch of the gfx950 kernels.
+//
+// Runtime rules from the "Oxide Infer" README (sections "One execution model"
+// and "Providers"): the caller selects the stream; read and write regions are
+// typed and checked for span, alignment, aliasing and capacity before anything
+// is enqueued; workspace requirements are explicit; device-detected failures
+// are typed status codes; enqueue neither tunes nor falls back silently.
+// Every check below runs on the host before the first HIP call, so a rejected
+// call touches no device state.
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/oxa.h"
+#include "kernels.h"
+
+namespace {
+
+struct Region {
+  const void* ptr;
+  uint64_t bytes;
+};
+
+bool overlaps(const Region& a, const Region& b) {
+  if (a.ptr == nullptr || b.ptr == nullptr || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.ptr), b0 = reinterpret_cast<uintptr_t>(b.ptr);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+bool aligned(const void* p, uintptr_t a) {
+  return p == nullptr || (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+// Outputs must not overlap any input or one another.
+bool any_alias(const Region* outs, int nout, const Region* ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlaps(outs[i], ins[j])) return true;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlaps(outs[i], outs[j])) return true;
+  }
+  return false;
+}
+
+constexpr uint64_t kRowBytes = OXA_HEAD_DIM * 2;  // one bf16 head row
+constexpr int kMaxGridYZ = 65535;
+
+oxa_status check_heads(int32_t hq, int32_t hkv, int32_t head_dim) {
+  if (head_dim != OXA_HEAD_DIM) return OXA_ERR_UNSUPPORTED;
+  if (hq < 1 || hkv < 1 || hq % hkv != 0) return OXA_ERR_SHAPE;
+  return OXA_OK;
+}
+
+oxa_status check_paging(int32_t page_size, int32_t layout, int32_t num_pages,
+                        int32_t num_page_entries) {
+  if (page_size != OXA_PAGE_SIZE) return OXA_ERR_UNSUPPORTED;
+  if (layout != OXA_LAYOUT_NHD && layout != OXA_LAYOUT_HND) return OXA_ERR_UNSUPPORTED;
+  if (num_pages < 1 || num_page_entries < 0) return OXA_ERR_SHAPE;
+  return OXA_OK;
+}
+
+oxa_status launch_status(hipError_t e) { return e == hipSuccess ? OXA_OK : OXA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t oxa_abi_version(void) { return OXA_ABI_VERSION; }
+
+const char* oxa_status_string(int32_t code) {
+  switch (code) {
+    case OXA_OK: return "OXA_OK";
+    case OXA_ERR_NULL: return "OXA_ERR_NULL";
+    case OXA_ERR_UNSUPPORTED: return "OXA_ERR_UNSUPPORTED";
+    case OXA_ERR_SHAPE: return "OXA_ERR_SHAPE";
+    case OXA_ERR_ALIGN: return "OXA_ERR_ALIGN";
+    case OXA_ERR_ALIAS: return "OXA_ERR_ALIAS";
+    case OXA_ERR_WORKSPACE: return "OXA_ERR_WORKSPACE";
+    case OXA_ERR_LAUNCH: return "OXA_ERR_LAUNCH";
+    case OXA_DEV_PAGE_RANGE: return "OXA_DEV_PAGE_RANGE";
+    case OXA_DEV_INDPTR: return "OXA_DEV_INDPTR";
+    case OXA_DEV_SEQ_LEN: return "OXA_DEV_SEQ_LEN";
+    case OXA_DEV_CAUSAL: return "OXA_DEV_CAUSAL";
+    case OXA_DEV_NOT_EXCLUSIVE: return "OXA_DEV_NOT_EXCLUSIVE";
+    case OXA_DEV_CAPACITY: return "OXA_DEV_CAPACITY";
+    case OXA_DEV_BATCH_INDEX: return "OXA_DEV_BATCH_INDEX";
+    default: return "unknown";
+  }
+}
+
+// ---------------------------------------------------------------- append
+
+oxa_status oxa_paged_append_rope(hipStream_t stream, const uint16_t* q_in, uint16_t* q_out,
+                                 int32_t num_qo_heads, const uint16_t* k_in,
+                                 const uint16_t* v_in, int32_t num_kv_heads, int32_t head_dim,
+                                 const int32_t* batch_indices, const int32_t* positions,
+                                 int32_t nnz, uint16_t* k_pages, uint16_t* v_pages,
+                                 int32_t num_pages, int32_t page_size, int32_t layout,
+                                 const int32_t* page_indptr, int32_t batch,
+                                 const int32_t* page_indices, int32_t num_page_entries,
+                                 const int32_t* page_refcounts, float rope_theta,
+                                 int32_t* status) {
+  if (!k_in || !v_in || !batch_indices || !positions || !k_pages || !v_pages || !page_indptr ||
+      !page_indices || !page_refcounts || !status)
+    return OXA_ERR_NULL;
+  if ((q_in == nullptr) != (q_out == nullptr)) return OXA_ERR_NULL;
+  const bool has_q = q_in != nullptr;
+  if (head_dim != OXA_HEAD_DIM) return OXA_ERR_UNSUPPORTED;
+  if (num_kv_heads < 1 || (has_q && num_qo_heads < 1)) return OXA_ERR_SHAPE;
+  if (oxa_status s = check_paging(page_size, layout, num_pages, num_page_entries)) return s;
+  if (nnz < 0 || batch < 1) return OXA_ERR_SHAPE;
+  if (!(rope_theta > 0.f) || !std::isfinite(rope_theta)) return OXA_ERR_SHAPE;
+  if (!aligned(q_in, 16) || !aligned(q_out, 16) || !aligned(k_in, 16) || !aligned(v_in, 16) ||
+      !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(batch_indices, 4) ||
+      !aligned(positions, 4) || !aligned(page_indptr, 4) || !aligned(page_indices, 4) ||
+      !aligned(page_refcounts, 4) || !aligned(status, 4))
+    return OXA_ERR_ALIGN;
+
+  const uint64_t n = (uint64_t)nnz;
+  const uint64_t qbytes = has_q ? n * (uint64_t)num_qo_heads * kRowBytes : 0;
+  const uint64_t pool = (uint64_t)num_pages * OXA_PAGE_SIZE * (uint64_t)num_kv_heads * kRowBytes;
+  const Region ins[] = {{q_in, qbytes},
+                        {k_in, n * num_kv_heads * kRowBytes},
+                        {v_in, n * num_kv_heads * kRowBytes},
+                        {batch_indices, n * 4},
+                        {positions, n * 4},
+                        {page_indptr, ((uint64_t)batch + 1) * 4},
+                        {page_indices, (uint64_t)num_page_entries * 4},
+                        {page_refcounts, (uint64_t)num_pages * 4}};
+  // q_out == q_in (exactly) is the in-place form; any other overlap is rejected
+  const bool in_place = has_q && q_out == q_in;
+  const Region outs[] = {{k_pages, pool}, {v_pages, pool}, {status, 8},
+                         {in_place ? nullptr : q_out, qbytes}};
+  if (any_alias(outs, 4, ins, 8)) return OXA_ERR_ALIAS;
+  if (in_place) {
+    const Region qr{q_in, qbytes};
+    for (int i = 1; i < 8; ++i)
+      if (overlaps(qr, ins[i])) return OXA_ERR_ALIAS;
+    for (int i = 0; i < 3; ++i)
+      if (overlaps(qr, outs[i])) return OXA_ERR_ALIAS;
+  }
+
+  oxa::AppendLaunch a;
+  a.q_in = q_in;
+  a.q_out = q_out;
+  a.k_in = k_in;
+  a.v_in = v_in;
+  a.batch_indices = batch_indices;
+  a.positions = positions;
+  a.k_pages = k_pages;
+  a.v_pages = v_pages;
+  a.page_indptr = page_indptr;
+  a.page_indices = page_indices;
+  a.page_refcounts = page_refcounts;
+  a.status = status;
+  a.hq = has_q ? num_qo_heads : 0;
+  a.hkv = num_kv_heads;
+  a.nnz = nnz;
+  a.num_pages = num_pages;
+  a.layout = layout;
+  a.batch = batch;
+  a.num_page_entries = num_page_entries;
+  for (int i = 0; i < 64; ++i)
+    a.inv_freq[i] = std::pow((double)rope_theta, -2.0 * (double)i / (double)OXA_HEAD_DIM);
+  return launch_status(oxa::launch_paged_append_rope(a, stream));
+}
+
+// ---------------------------------------------------------------- decode
+
+size_t oxa_paged_decode_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t head_dim,
+                                        int32_t num_partitions) {
+  if (batch < 1 || num_qo_heads < 1 || head_dim != OXA_HEAD_DIM || num_partitions <= 1) return 0;
+  const uint64_t rows = (uint64_t)batch * num_qo_heads * num_partitions;
+  return (size_t)(rows * OXA_HEAD_DIM * 4 + rows * 4);
+}
+
+oxa_status oxa_paged_decode(hipStream_t stream, const uint16_t* q, int32_t batch,
+                            int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                            const uint16_t* k_pages, const uint16_t* v_pages, int32_t num_pages,
+                            int32_t page_size, int32_t layout, const int32_t* page_indptr,
+                            const int32_t* page_indices, int32_t num_page_entries,
+                            const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                            int32_t num_partitions, void* workspace, size_t workspace_bytes,
+                            uint16_t* o, float* lse, int32_t* status) {
+  if (!q || !k_pages || !v_pages || !page_indptr || !page_indices || !seq_lens || !o)
+    return OXA_ERR_NULL;
+  if (oxa_status s = check_heads(num_qo_heads, num_kv_heads, head_dim)) return s;
+  if (oxa_status s = check_paging(page_size, layout, num_pages, num_page_entries)) return s;
+  if (batch < 1 || batch > kMaxGridYZ || max_seq_len < 1 || num_partitions < 1 ||
+      num_partitions > 1024 || !std::isfinite(sm_scale))
+    return OXA_ERR_SHAPE;
+  const int32_t group = num_qo_heads / num_kv_heads;
+  if ((uint64_t)num_kv_heads * (uint64_t)((group + 31) / 32) > (uint64_t)kMaxGridYZ)
+    return OXA_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(o, 16) ||
+      !aligned(workspace, 16) || !aligned(lse, 4) || !aligned(status, 4) ||
+      !aligned(page_indptr, 4) || !aligned(page_indices, 4) || !aligned(seq_lens, 4))
+    return OXA_ERR_ALIGN;
+  const size_t need = oxa_paged_decode_workspace_bytes(batch, num_qo_heads, head_dim,
+                                                       num_partitions);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return OXA_ERR_WORKSPACE;
+
+  const uint64_t B = (uint64_t)batch;
+  const uint64_t pool = (uint64_t)num_pages * OXA_PAGE_SIZE * (uint64_t)num_kv_heads * kRowBytes;
+  const Region ins[] = {{q, B * num_qo_heads * kRowBytes},
+                        {k_pages, pool},
+                        {v_pages, pool},
+                        {page_indptr, (B + 1) * 4},
+                        {page_indices, (uint64_t)num_page_entries * 4},
+                        {seq_lens, B * 4}};
+  const Region outs[] = {{o, B * num_qo_heads * kRowBytes},
+                         {lse, lse ? B * num_qo_heads * 4 : 0},
+                         {status, status ? B * 4 : 0},
+                         {workspace, need}};
+  if (any_alias(outs, 4, ins, 6)) return OXA_ERR_ALIAS;
+
+  oxa::DecodeLaunch a;
+  a.q = q;
+  a.k_pages = k_pages;
+  a.v_pages = v_pages;
+  a.page_indptr = page_indptr;
+  a.page_indices = page_indices;
+  a.seq_lens = seq_lens;
+  a.o = o;
+  a.lse = lse;
+  a.status = status;
+  a.ws_o = need ? static_cast<float*>(workspace) : nullptr;
+  a.ws_lse = need ? static_cast<float*>(workspace) + B * num_qo_heads * num_partitions * OXA_HEAD_DIM
+                  : nullptr;
+  a.batch = batch;
+  a.hq = num_qo_heads;
+  a.hkv = num_kv_heads;
+  a.layout = layout;
+  a.num_pages = num_pages;
+  a.num_page_entries = num_page_entries;
+  a.max_seq_len = max_seq_len;
+  a.num_partitions = num_partitions;
+  const int32_t max_pages = (max_seq_len + OXA_PAGE_SIZE - 1) / OXA_PAGE_SIZE;
+  a.chunk_pages = (max_pages + num_partitions - 1) / num_partitions;
+  a.sm_scale = sm_scale;
+  return launch_status(oxa::launch_paged_decode(a, stream));
+}
+
+// ---------------------------------------------------------------- prefill
+
+size_t oxa_ragged_prefill_workspace_bytes(int32_t, int32_t, int32_t, int32_t) { return 0; }
+size_t oxa_paged_prefill_workspace_bytes(int32_t, int32_t, int32_t, int32_t) { return 0; }
+
+namespace {
+
+// Query tiles of the prefill grid for the given head grouping (256 columns
+// per work-group, BM = 256 / min(group, 256) rows each).
+uint64_t prefill_tiles(int32_t hq, int32_t hkv, int32_t max_qo_len) {
+  const int32_t group = hq / hkv;
+  const int32_t gwg = group < 256 ? group : 256;
+  const int32_t bm = 256 / gwg;
+  return ((uint64_t)max_qo_len + bm - 1) / bm;
+}
+
+}  // namespace
+
+oxa_status oxa_ragged_prefill(hipStream_t stream, const uint16_t* q, const uint16_t* k,
+                              const uint16_t* v, const int32_t* qo_indptr,
+                              const int32_t* kv_indptr, int32_t batch, int32_t nnz_qo,
+                              int32_t nnz_kv, int32_t num_qo_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t max_qo_len, int32_t max_kv_len,
+                              int32_t causal, float sm_scale, void* workspace,
+                              size_t workspace_bytes, uint16_t* o, float* lse, int32_t* status) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!q || !k || !v || !qo_indptr || !kv_indptr || !o) return OXA_ERR_NULL;
+  if (oxa_status s = check_heads(num_qo_heads, num_kv_heads, head_dim)) return s;
+  if (batch < 1 || batch > kMaxGridYZ || nnz_qo < 0 || nnz_kv < 0 || max_qo_len < 1 ||
+      max_kv_len < 1 || !std::isfinite(sm_scale))
+    return OXA_ERR_SHAPE;
+  const int32_t group = num_qo_heads / num_kv_heads;
+  if (prefill_tiles(num_qo_heads, num_kv_heads, max_qo_len) > (uint64_t)kMaxGridYZ ||
+      (uint64_t)num_kv_heads * (uint64_t)((group + 255) / 256) > 0x7fffffffull)
+    return OXA_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(status, 4) || !aligned(qo_indptr, 4) || !aligned(kv_indptr, 4))
+    return OXA_ERR_ALIGN;
+  const uint64_t B = (uint64_t)batch;
+  const Region ins[] = {{q, (uint64_t)nnz_qo * num_qo_heads * kRowBytes},
+                        {k, (uint64_t)nnz_kv * num_kv_heads * kRowBytes},
+                        {v, (uint64_t)nnz_kv * num_kv_heads * kRowBytes},
+                        {qo_indptr, (B + 1) * 4},
+                        {kv_indptr, (B + 1) * 4}};
+  const Region outs[] = {{o, (uint64_t)nnz_qo * num_qo_heads * kRowBytes},
+                         {lse, lse ? (uint64_t)nnz_qo * num_qo_heads * 4 : 0},
+                         {status, status ? B * 4 : 0}};
+  if (any_alias(outs, 3, ins, 5)) return OXA_ERR_ALIAS;
+
+  oxa::PrefillLaunch a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.qo_indptr = qo_indptr;
+  a.kv_indptr = kv_indptr;
+  a.o = o;
+  a.lse = lse;
+  a.status = status;
+  a.paged = 0;
+  a.layout = 0;
+  a.batch = batch;
+  a.nnz_qo = nnz_qo;
+  a.nnz_kv = nnz_kv;
+  a.hq = num_qo_heads;
+  a.hkv = num_kv_heads;
+  a.max_qo_len = max_qo_len;
+  a.max_kv_len = max_kv_len;
+  a.causal = causal != 0;
+  a.sm_scale = sm_scale;
+  return launch_status(oxa::launch_prefill(a, stream));
+}
+
+oxa_status oxa_paged_prefill(hipStream_t stream, const uint16_t* q, const int32_t* qo_indptr,
+                             const uint16_t* k_pages, const uint16_t* v_pages, int32_t num_pages,
+                             int32_t page_size, int32_t layout, const int32_t* page_indptr,
+                             const int32_t* page_indices, int32_t num_page_entries,
+                             const int32_t* seq_lens, int32_t batch, int32_t nnz_qo,
+                             int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t max_qo_len, int32_t max_seq_len, int32_t causal,
+                             float sm_scale, void* workspace, size_t workspace_bytes,
+                             uint16_t* o, float* lse, int32_t* status) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!q || !qo_indptr || !k_pages || !v_pages || !page_indptr || !page_indices || !seq_lens ||
+      !o)
+    return OXA_ERR_NULL;
+  if (oxa_status s = check_heads(num_qo_heads, num_kv_heads, head_dim)) return s;
+  if (oxa_status s = check_paging(page_size, layout, num_pages, num_page_entries)) return s;
+  if (batch < 1 || batch > kMaxGridYZ || nnz_qo < 0 || max_qo_len < 1 || max_seq_len < 1 ||
+      !std::isfinite(sm_scale))
+    return OXA_ERR_SHAPE;
+  const int32_t group = num_qo_heads / num_kv_heads;
+  if (prefill_tiles(num_qo_heads, num_kv_heads, max_qo_len) > (uint64_t)kMaxGridYZ ||
+      (uint64_t)num_kv_heads * (uint64_t)((group + 255) / 256) > 0x7fffffffull)
+    return OXA_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(status, 4) || !aligned(qo_indptr, 4) ||
+      !aligned(page_indptr, 4) || !aligned(page_indices, 4) || !aligned(seq_lens, 4))
+    return OXA_ERR_ALIGN;
+  const uint64_t B = (uint64_t)batch;
+  const uint64_t pool = (uint64_t)num_pages * OXA_PAGE_SIZE * (uint64_t)num_kv_heads * kRowBytes;
+  const Region ins[] = {{q, (uint64_t)nnz_qo * num_qo_heads * kRowBytes},
+                        {k_pages, pool},
+                        {v_pages, pool},
+                        {qo_indptr, (B + 1) * 4},
+                        {page_indptr, (B + 1) * 4},
+                        {page_indices, (uint64_t)num_page_entries * 4},
+                        {seq_lens, B * 4}};
+  const Region outs[] = {{o, (uint64_t)nnz_qo * num_qo_heads * kRowBytes},
+                         {lse, lse ? (uint64_t)nnz_qo * num_qo_heads * 4 : 0},
+                         {status, status ? B * 4 : 0}};
+  if (any_alias(outs, 3, ins, 7)) return OXA_ERR_ALIAS;
+
+  oxa::PrefillLaunch a = {};
+  a.q = q;
+  a.k = k_pages;
+  a.v = v_pages;
+  a.qo_indptr = qo_indptr;
+  a.page_indptr = page_indptr;
+  a.page_indices = page_indices;
+  a.seq_lens = seq_lens;
+  a.o = o;
+  a.lse = lse;
+  a.status = status;
+  a.paged = 1;
+  a.layout = layout;
+  a.batch = batch;
+  a.nnz_qo = nnz_qo;
+  a.hq = num_qo_heads;
+  a.hkv = num_kv_heads;
+  a.max_qo_len = max_qo_len;
+  a.max_kv_len = max_seq_len;
+  a.causal = causal != 0;
+  a.num_pages = num_pages;
+  a.num_page_entries = num_page_entries;
+  a.sm_scale = sm_scale;
+  return launch_status(oxa::launch_prefill(a, stream));
+}
+
+}  // extern "C"

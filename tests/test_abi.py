@@ -1,0 +1,42 @@
+"""The C-ABI library loads and exports every entry point include/oxa.h declares (no GPU needed)."""
+import ctypes
+import os
+import re
+
+from tests.lib_loader import ensure_built
+
+import paged_attention_02_amd as oxa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "oxa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(oxa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ensure_built()
+    names = declared_functions()
+    assert {"oxa_paged_append_rope", "oxa_paged_decode", "oxa_ragged_prefill",
+            "oxa_paged_prefill"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in oxa.SIGNATURES, f"binding lacks a signature for {n}"
+
+
+def test_abi_version_and_status_strings():
+    lib = ensure_built()
+    assert lib.oxa_abi_version() == 1
+    assert oxa.status_string(0) == "OXA_OK"
+    assert oxa.status_string(20) == "OXA_DEV_NOT_EXCLUSIVE"
+    assert oxa.status_string(999) == "unknown"
+
+
+def test_workspace_queries():
+    ensure_built()
+    assert oxa.oxa_paged_decode_workspace_bytes(8, 32, 1) == 0
+    # the long MQA workload: 8 x 32 rows x 16 partitions x (128 + 1) floats
+    assert oxa.oxa_paged_decode_workspace_bytes(8, 32, 16) == 8 * 32 * 16 * 129 * 4 == 2113536
+    assert oxa.lib().oxa_ragged_prefill_workspace_bytes(4, 7680, 32, 128) == 0

@@ -1,0 +1,137 @@
+"""Host-side contract checks of the C ABI: each call below breaks one rule and
+must return the matching OXA_ERR_* code before touching the GPU.
+
+The pointers are fake (never dereferenced): validation rejects the call first.
+These tests do not run where a GPU is visible, so a validation bug can never
+turn one of them into a real launch.
+"""
+import pytest
+import torch
+
+from tests.lib_loader import ensure_built
+
+import paged_attention_02_amd as oxa
+
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(),
+                                reason="fake-pointer validation tests run on GPU-less hosts only")
+
+A = 1 << 32          # a 16-byte aligned fake address space, regions far apart
+GAP = 1 << 30
+
+
+def addr(i):
+    return A + i * GAP
+
+
+def decode_args(**over):
+    args = dict(stream=None, q=addr(0), batch=2, hq=8, hkv=2, head_dim=128, k=addr(1), v=addr(2),
+                num_pages=10, page_size=16, layout=0, indptr=addr(3), indices=addr(4),
+                num_entries=6, seq_lens=addr(5), max_seq_len=64, scale=0.088, P=1,
+                ws=None, ws_bytes=0, o=addr(6), lse=None, status=None)
+    args.update(over)
+    return list(args.values())
+
+
+def call_decode(**over):
+    return ensure_built().oxa_paged_decode(*decode_args(**over))
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), oxa.OXA_ERR_NULL),
+    (dict(o=None), oxa.OXA_ERR_NULL),
+    (dict(head_dim=64), oxa.OXA_ERR_UNSUPPORTED),
+    (dict(page_size=32), oxa.OXA_ERR_UNSUPPORTED),
+    (dict(layout=2), oxa.OXA_ERR_UNSUPPORTED),
+    (dict(hq=6, hkv=4), oxa.OXA_ERR_SHAPE),
+    (dict(batch=0), oxa.OXA_ERR_SHAPE),
+    (dict(max_seq_len=0), oxa.OXA_ERR_SHAPE),
+    (dict(P=0), oxa.OXA_ERR_SHAPE),
+    (dict(P=1025), oxa.OXA_ERR_SHAPE),
+    (dict(num_pages=0), oxa.OXA_ERR_SHAPE),
+    (dict(scale=float("nan")), oxa.OXA_ERR_SHAPE),
+    (dict(q=addr(0) + 8), oxa.OXA_ERR_ALIGN),
+    (dict(seq_lens=addr(5) + 2), oxa.OXA_ERR_ALIGN),
+    (dict(P=4), oxa.OXA_ERR_WORKSPACE),
+    (dict(P=4, ws=addr(7), ws_bytes=100), oxa.OXA_ERR_WORKSPACE),
+    (dict(o=addr(0) + 512), oxa.OXA_ERR_ALIAS),            # o overlaps q
+    (dict(lse=addr(1) + 4096), oxa.OXA_ERR_ALIAS),         # lse inside the K pool
+    (dict(status=addr(6) + 16), oxa.OXA_ERR_ALIAS),        # status inside o
+    (dict(P=4, ws=addr(2), ws_bytes=1 << 20), oxa.OXA_ERR_ALIAS),  # workspace over the V pool
+])
+def test_decode_rejections(over, code):
+    assert call_decode(**over) == code
+
+
+def call_ragged(**over):
+    args = dict(stream=None, q=addr(0), k=addr(1), v=addr(2), qo=addr(3), kv=addr(4), batch=2,
+                nnz_qo=100, nnz_kv=100, hq=8, hkv=2, head_dim=128, max_qo=64, max_kv=64,
+                causal=1, scale=0.088, ws=None, ws_bytes=0, o=addr(5), lse=None, status=None)
+    args.update(over)
+    return ensure_built().oxa_ragged_prefill(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(k=None), oxa.OXA_ERR_NULL),
+    (dict(head_dim=256), oxa.OXA_ERR_UNSUPPORTED),
+    (dict(hq=8, hkv=3), oxa.OXA_ERR_SHAPE),
+    (dict(nnz_qo=-1), oxa.OXA_ERR_SHAPE),
+    (dict(max_qo=0), oxa.OXA_ERR_SHAPE),
+    (dict(max_qo=1 << 30), oxa.OXA_ERR_SHAPE),       # more query tiles than the grid allows
+    (dict(v=addr(2) + 4), oxa.OXA_ERR_ALIGN),
+    (dict(o=addr(1) + 256), oxa.OXA_ERR_ALIAS),      # o overlaps k
+    (dict(status=addr(4)), oxa.OXA_ERR_ALIAS),       # status over kv_indptr
+])
+def test_ragged_rejections(over, code):
+    assert call_ragged(**over) == code
+
+
+def call_paged_prefill(**over):
+    args = dict(stream=None, q=addr(0), qo=addr(1), k=addr(2), v=addr(3), num_pages=10,
+                page_size=16, layout=1, indptr=addr(4), indices=addr(5), num_entries=10,
+                seq_lens=addr(6), batch=2, nnz_qo=50, hq=4, hkv=4, head_dim=128, max_qo=64,
+                max_seq=64, causal=1, scale=0.088, ws=None, ws_bytes=0, o=addr(7), lse=None,
+                status=None)
+    args.update(over)
+    return ensure_built().oxa_paged_prefill(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(seq_lens=None), oxa.OXA_ERR_NULL),
+    (dict(layout=-1), oxa.OXA_ERR_UNSUPPORTED),
+    (dict(num_entries=-1), oxa.OXA_ERR_SHAPE),
+    (dict(max_seq=0), oxa.OXA_ERR_SHAPE),
+    (dict(o=addr(7) + 2), oxa.OXA_ERR_ALIGN),
+    (dict(lse=addr(3) + 8), oxa.OXA_ERR_ALIAS),
+])
+def test_paged_prefill_rejections(over, code):
+    assert call_paged_prefill(**over) == code
+
+
+def call_append(**over):
+    args = dict(stream=None, q_in=addr(0), q_out=addr(1), hq=8, k_in=addr(2), v_in=addr(3), hkv=2,
+                head_dim=128, bidx=addr(4), pos=addr(5), nnz=20, kp=addr(6), vp=addr(7),
+                num_pages=10, page_size=16, layout=0, indptr=addr(8), batch=2, indices=addr(9),
+                num_entries=10, refc=addr(10), theta=10000.0, status=addr(11))
+    args.update(over)
+    return ensure_built().oxa_paged_append_rope(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(status=None), oxa.OXA_ERR_NULL),
+    (dict(refc=None), oxa.OXA_ERR_NULL),
+    (dict(q_out=None), oxa.OXA_ERR_NULL),               # q_in without q_out
+    (dict(head_dim=96), oxa.OXA_ERR_UNSUPPORTED),
+    (dict(page_size=8), oxa.OXA_ERR_UNSUPPORTED),
+    (dict(nnz=-3), oxa.OXA_ERR_SHAPE),
+    (dict(batch=0), oxa.OXA_ERR_SHAPE),
+    (dict(theta=0.0), oxa.OXA_ERR_SHAPE),
+    (dict(theta=float("inf")), oxa.OXA_ERR_SHAPE),
+    (dict(k_in=addr(2) + 8), oxa.OXA_ERR_ALIGN),
+    (dict(pos=addr(5) + 1), oxa.OXA_ERR_ALIGN),
+    (dict(q_out=addr(0) + 256), oxa.OXA_ERR_ALIAS),     # partial overlap with q_in
+    (dict(kp=addr(2)), oxa.OXA_ERR_ALIAS),              # K pool over k_in
+    (dict(status=addr(6) + 64), oxa.OXA_ERR_ALIAS),     # status inside the K pool
+    (dict(vp=addr(6) + 1024), oxa.OXA_ERR_ALIAS),       # V pool overlaps K pool
+])
+def test_append_rejections(over, code):
+    assert call_append(**over) == code
