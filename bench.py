@@ -1,0 +1,393 @@
+"""Benchmark: paged-decode HBM GB/s + causal-prefill TFLOPS on one MI355X.
+
+One JSON line on stdout.  The timed step is one paged batch decode over the
+batch-32 GQA4 workload (32 q / 8 kv heads, head dim 128, page size 16,
+seq_lens uniform in [512, 4096], pages shuffled in a shared NHD pool, seed
+1002); `value` is its algorithmic HBM bytes / measured step time.  Every step
+reads a different copy of the KV pool (copies rotate, > 1 GiB apart), so each
+step streams its KV from HBM rather than from the 256 MB last-level cache.
+
+The same run also measures, as extra fields, the long-context causal prefill
+(RoPE + exclusive paged append of 2 x 16384 tokens, then paged causal prefill
+over those pages; TFLOPS against the bf16 matrix-core peak), the ragged GQA4
+prefill, the long MQA split-K decode and the tiny MHA decode.  Kernel-level
+durations come from HIP events on the launching stream; the oracle's CPU
+throughput on the decode workload is reported as `cpu_baseline`.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only ROW]
+       [--no-cpu-baseline] [--decode-partitions P]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, TFLOP/s
+ROWS = ("decode", "decode_mha", "decode_mqa", "prefill_ragged", "append", "prefill_paged")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+
+
+class LaunchTimer:
+    """Per-launch HIP event pairs on the given stream plus a whole-region pair."""
+
+    def __init__(self, torch, stream, n):
+        self.torch = torch
+        self.stream = stream
+        self.pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(n)]
+
+    def run(self, fn, n):
+        for i in range(n):
+            a, b = self.pairs[i]
+            a.record(self.stream)
+            fn(i)
+            b.record(self.stream)
+
+    def launch_ms(self, n):
+        self.torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in self.pairs[:n]])
+
+
+def decode_bytes(case):
+    """Algorithmic HBM bytes of one paged decode: K+V rows of every token of every
+    sequence and kv head, q in, o out, and the page table read."""
+    kv = case.kv
+    hkv = kv.num_kv_heads
+    B, hq, d = case.q.shape
+    tokens = int(np.sum(kv.seq_lens.astype(np.int64)))
+    pages = int(np.sum((kv.seq_lens.astype(np.int64) + 15) // 16))
+    return tokens * hkv * d * 2 * 2 + 2 * B * hq * d * 2 + pages * 4 + (2 * B + 1) * 4
+
+
+def causal_flops(qo_lens, kv_lens, hq, d=128):
+    """Matrix flops of causal attention (QK^T and PV) over the visible pairs
+    (bottom-right alignment): 4 * d * hq per (query, key) pair."""
+    pairs = 0
+    for q, k in zip(qo_lens, kv_lens):
+        q, k = int(q), int(k)
+        pairs += q * (k - q + 1) + q * (q - 1) // 2
+    return 4 * d * hq * pairs
+
+
+def source_hash(name):
+    path = os.path.join(ROOT, "paged_attention_02_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def profiled_traffic(kernel_file, profile_name):
+    """HBM bytes per launch recorded from rocprofv3 counters, if the kernel source
+    has not changed since (the summary records the source hash)."""
+    path = os.path.join(ROOT, "profiles", profile_name)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source sha256\[:16\]:\s*([0-9a-f]{16})", text)
+    m_bytes = re.search(r"HBM bytes per launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(kernel_file):
+        return None
+    return float(m_bytes.group(1))
+
+
+# ----------------------------------------------------------------------------- rows
+
+def bench_decode(torch, oxa, W, case, steps, warmup, copies_bytes=1 << 30, partitions=None):
+    """Time paged decode over `case`, rotating pool copies so each step is cold."""
+    kv = case.kv
+    B, hq, _ = case.q.shape
+    P = case.num_partitions if partitions is None else partitions
+    pool_bytes = kv.k_pool.nbytes * 2
+    ncopies = max(1, min(16, math.ceil(copies_bytes / max(pool_bytes, 1)) + 1))
+    kps = [dev(kv.k_pool)]
+    vps = [dev(kv.v_pool)]
+    for _ in range(ncopies - 1):
+        kps.append(kps[0].clone())
+        vps.append(vps[0].clone())
+    q = dev(case.q)
+    o = torch.empty_like(q)
+    indptr, ids, lens = dev(kv.page_indptr), dev(kv.page_indices), dev(kv.seq_lens)
+    nbytes = oxa.oxa_paged_decode_workspace_bytes(B, hq, P)
+    ws = torch.empty(max(nbytes, 4) // 4, dtype=torch.float32, device="cuda") if nbytes else None
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        j = i % ncopies
+        rc = oxa.oxa_paged_decode(q, kps[j], vps[j], indptr, ids, lens, o,
+                                  max_seq_len=case.max_seq_len, sm_scale=case.sm_scale,
+                                  layout=kv.layout, num_kv_heads=kv.num_kv_heads,
+                                  num_partitions=P, workspace=ws)
+        if rc != 0:
+            raise RuntimeError(oxa.status_string(rc))
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    timer = LaunchTimer(torch, stream, steps)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    timer.run(lambda i: call(i + warmup), steps)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    launch = timer.launch_ms(steps)
+    total_ms = t_start.elapsed_time(t_end)
+    return dict(total_ms=total_ms, launch_ms=launch, bytes=decode_bytes(case), copies=ncopies,
+                partitions=P)
+
+
+def bench_prefill_ragged(torch, oxa, case, iters, warmup):
+    q, k, v = dev(case.q), dev(case.k), dev(case.v)
+    o = torch.empty_like(q)
+    qi, ki = dev(case.qo_indptr), dev(case.kv_indptr)
+    qlens = np.diff(case.qo_indptr)
+    klens = np.diff(case.kv_indptr)
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        rc = oxa.oxa_ragged_prefill(q, k, v, qi, ki, o, max_qo_len=int(qlens.max()),
+                                    max_kv_len=int(klens.max()), sm_scale=case.sm_scale,
+                                    causal=True)
+        if rc != 0:
+            raise RuntimeError(oxa.status_string(rc))
+
+    for i in range(warmup):
+        call(i)
+    timer = LaunchTimer(torch, stream, iters)
+    timer.run(call, iters)
+    ms = timer.launch_ms(iters)
+    return dict(launch_ms=ms, flops=causal_flops(qlens, klens, case.num_qo_heads))
+
+
+def bench_append_and_paged_prefill(torch, oxa, case, iters, warmup):
+    kv = case.kv
+    q_in = dev(case.q)
+    q_rot = torch.empty_like(q_in)
+    k_in, v_in = dev(case.k), dev(case.v)
+    bi, pos = dev(case.batch_indices), dev(case.positions)
+    kp, vp = dev(kv.k_pool), dev(kv.v_pool)
+    indptr, ids, rc_t = dev(kv.page_indptr), dev(kv.page_indices), dev(case.page_refcounts)
+    status = torch.zeros(2, dtype=torch.int32, device="cuda")
+    lens = dev(kv.seq_lens)
+    qoi = dev(case.qo_indptr)
+    o = torch.empty_like(q_in)
+    stream = torch.cuda.current_stream()
+    hkv = kv.num_kv_heads
+
+    def append(i):
+        rc = oxa.oxa_paged_append_rope(q_in, q_rot, k_in, v_in, bi, pos, kp, vp, indptr, ids, rc_t,
+                                       status, layout=kv.layout, rope_theta=case.rope_theta)
+        if rc != 0:
+            raise RuntimeError(oxa.status_string(rc))
+
+    max_len = int(kv.seq_lens.max())
+
+    def prefill(i):
+        rc = oxa.oxa_paged_prefill(q_rot, qoi, kp, vp, indptr, ids, lens, o, max_qo_len=max_len,
+                                   max_seq_len=max_len, sm_scale=case.sm_scale, layout=kv.layout,
+                                   num_kv_heads=hkv, causal=True)
+        if rc != 0:
+            raise RuntimeError(oxa.status_string(rc))
+
+    for i in range(warmup):
+        append(i)
+        prefill(i)
+    ta = LaunchTimer(torch, stream, iters)
+    ta.run(append, iters)
+    a_ms = ta.launch_ms(iters)
+    tp = LaunchTimer(torch, stream, iters)
+    tp.run(prefill, iters)
+    p_ms = tp.launch_ms(iters)
+    torch.cuda.synchronize()
+    assert status.cpu().tolist() == [0, -1]
+    nnz, hq, d = case.q.shape
+    append_bytes = (nnz * hq * d * 2 * 2            # q read + q_out write
+                    + nnz * hkv * d * 2 * 2 * 2     # k, v read + written into pages
+                    + nnz * 4 * 2                   # positions + batch indices
+                    + nnz // 16 * 4 * 2)            # page ids + refcounts, once per page
+    qlens = np.diff(case.qo_indptr)
+    return dict(append_ms=a_ms, append_bytes=append_bytes, prefill_ms=p_ms,
+                prefill_flops=causal_flops(qlens, kv.seq_lens, hq))
+
+
+def cpu_baseline(case, budget_s=10.0):
+    """The oracle's paged decode of the whole workload, repeated for ~budget_s,
+    with its BLAS pool held to one thread."""
+    from oracle import attention as A
+    from threadpoolctl import threadpool_limits
+    kv = case.kv
+    reps, t0 = 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            A.paged_decode(case.q, kv.k_pool, kv.v_pool, kv.layout, kv.page_indptr,
+                           kv.page_indices, kv.seq_lens, case.sm_scale)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+    gbs = decode_bytes(case) * reps / el / 1e9
+    return dict(value=round(gbs, 3), unit="GB/s", cores=1, kind="oracle",
+                sample=f"whole batch-32 GQA4 decode workload, {reps} repetitions in {el:.1f} s, "
+                       "numpy float64, BLAS held to 1 thread")
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", choices=ROWS, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-partitions", type=int, default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this library's hot path runs on a single MI355X "
+              "(multi-GPU sharding is a design note, not built); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_attention_02_amd as oxa
+    import workloads as W
+    if not os.path.exists(oxa.LIB_PATH):
+        from paged_attention_02_amd import build as _b
+        _b.build()
+    oxa.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    only = args.only
+    out = {}
+
+    decode_P = args.decode_partitions
+    if decode_P is None:
+        decode_P = int(os.environ.get("OXA_BENCH_DECODE_P", "1"))
+    case2 = W.decode_gqa4_batch(num_partitions=decode_P)
+    if only in (None, "decode"):
+        log("decode: batch-32 GQA4")
+        out["decode"] = bench_decode(torch, oxa, W, case2, args.steps, args.warmup)
+    if only in (None, "decode_mha"):
+        log("decode_mha: batch-1 MHA, 256 tokens")
+        out["decode_mha"] = bench_decode(torch, oxa, W, W.decode_mha_small(), 100, 10,
+                                         copies_bytes=1 << 30)
+    if only in (None, "decode_mqa"):
+        log("decode_mqa: batch-8 MQA, 32768 tokens, 16 partitions")
+        out["decode_mqa"] = bench_decode(torch, oxa, W, W.decode_mqa_long(), 30, 5)
+    if only in (None, "prefill_ragged"):
+        log("prefill_ragged: GQA4 {512,1024,2048,4096}")
+        out["prefill_ragged"] = bench_prefill_ragged(torch, oxa, W.ragged_gqa4_prefill(), 20, 3)
+    if only in (None, "append", "prefill_paged"):
+        log("append + paged prefill: 2 x 16384 tokens")
+        out["long"] = bench_append_and_paged_prefill(torch, oxa, W.rope_append_prefill(), 10, 2)
+
+    line = {
+        "metric": "paged-decode HBM GB/s (% peak) + causal-prefill TFLOPS (% bf16 MFMA peak)",
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+    }
+    if "decode" in out:
+        r = out["decode"]
+        step_ms = r["total_ms"] / args.steps
+        lm = float(np.mean(r["launch_ms"]))
+        achieved = r["bytes"] / (lm * 1e-3) / 1e9
+        traffic = profiled_traffic("decode.hip", "paged_decode_gqa4_batch32.md")
+        line.update({
+            "value": round(r["bytes"] / (step_ms * 1e-3) / 1e9, 1),
+            "ms_per_step": round(step_ms, 5),
+            "config": {"workload": "paged batch decode GQA4: batch 32, 32 q / 8 kv heads, "
+                                   "head_dim 128, page 16, seq_lens U[512,4096] (seed 1002), "
+                                   "shuffled NHD pool, bf16 N(0,1)",
+                       "seq_tokens": int(case2.kv.seq_lens.sum()),
+                       "num_partitions": r["partitions"],
+                       "pool_copies_rotated": r["copies"],
+                       "algorithmic_bytes_per_step": r["bytes"]},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": traffic,
+                         "kernel": "paged_decode_kernel" + ("" if r["partitions"] == 1 else
+                                                            " + merge_partials_kernel"),
+                         "launch_us_mean": round(lm * 1e3, 2),
+                         "launch_us_p10_p50_p90": [round(float(x) * 1e3, 2) for x in
+                                                   np.percentile(r["launch_ms"], [10, 50, 90])]},
+        })
+    rows = {}
+    if "decode_mha" in out:
+        r = out["decode_mha"]
+        lm = float(np.mean(r["launch_ms"]))
+        rows["decode_mha_b1_l256"] = {"us": round(lm * 1e3, 2),
+                                      "GB/s": round(r["bytes"] / (lm * 1e-3) / 1e9, 1)}
+    if "decode_mqa" in out:
+        r = out["decode_mqa"]
+        lm = float(np.mean(r["launch_ms"]))
+        gbs = r["bytes"] / (lm * 1e-3) / 1e9
+        rows["decode_mqa_splitk_b8_l32768_p16"] = {
+            "us": round(lm * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes": r["bytes"]}
+    if "prefill_ragged" in out:
+        r = out["prefill_ragged"]
+        lm = float(np.mean(r["launch_ms"]))
+        tf = r["flops"] / (lm * 1e-3) / 1e12
+        rows["prefill_ragged_gqa4_4seq"] = {"us": round(lm * 1e3, 1), "TFLOPS": round(tf, 1),
+                                            "frac_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                                            "flops": r["flops"]}
+    if "long" in out:
+        r = out["long"]
+        am = float(np.mean(r["append_ms"]))
+        pm = float(np.mean(r["prefill_ms"]))
+        gbs = r["append_bytes"] / (am * 1e-3) / 1e9
+        tf = r["prefill_flops"] / (pm * 1e-3) / 1e12
+        rows["rope_append_2x16384"] = {"us": round(am * 1e3, 1), "GB/s": round(gbs, 1),
+                                       "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                                       "bytes": r["append_bytes"]}
+        rows["prefill_paged_gqa4_2x16384"] = {"us": round(pm * 1e3, 1), "TFLOPS": round(tf, 1),
+                                              "frac_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                                              "flops": r["prefill_flops"]}
+        traffic = profiled_traffic("prefill.hip", "prefill_paged_gqa4_2x16384.md")
+        line["prefill"] = {"metric": "causal-prefill TFLOPS", "value": round(tf, 1),
+                           "unit": "TFLOP/s",
+                           "workload": "paged causal prefill GQA4, 2 x 16384 tokens, 32 q / 8 kv "
+                                       "heads, pages filled by the fused RoPE + append",
+                           "roofline": {"bound": "mfma", "achieved": round(tf, 1),
+                                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                        "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                                        "traffic": traffic, "kernel": "prefill_kernel"}}
+    line["rows"] = rows
+    if "value" not in line:
+        line.update({"value": None, "ms_per_step": None, "config": {"workload": only}})
+    if only is None and not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(case2)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
