@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, TFLOP/s
-ROWS = ("decode", "decode_mha", "decode_mqa", "prefill_ragged", "append", "prefill_paged")
+ROWS = ("decode", "decode_mha", "decode_mqa", "prefill_ragged", "append", "prefill_paged", "copy")
 
 
 def log(msg):
@@ -301,6 +301,17 @@ def main():
     if only in (None, "append", "prefill_paged"):
         log("append + paged prefill: 2 x 16384 tokens")
         out["long"] = bench_append_and_paged_prefill(torch, oxa, W.rope_append_prefill(), 10, 2)
+
+    if only == "copy":
+        # a plain device copy of known size: the reference for scaling the HBM
+        # byte counters (FETCH_SIZE / WRITE_SIZE) read under rocprofv3
+        n = 512 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 5 copies of {n} bytes")
 
     line = {
         "metric": "paged-decode HBM GB/s (% peak) + causal-prefill TFLOPS (% bf16 MFMA peak)",

@@ -52,8 +52,8 @@
  *          than its length needs; attention reads only the first
  *          ceil(len / 16).  num_page_entries is the length of page_indices.
  * Alignment. Every bf16 tensor and the workspace must be 16-byte aligned.
- * Softmax. f32 running max / sum / accumulator; outputs rounded to bf16
- *          (nearest-even).  lse (optional, may be NULL) is the natural-log
+ * Softmax. sm_scale must be finite and >= 0.  f32 running max / sum /
+ *          accumulator; outputs rounded to bf16 (nearest-even).  lse (optional, may be NULL) is the natural-log
  *          log-sum-exp of the scaled scores of each (query row, q head).
  */
 #ifndef OXA_H
@@ -78,7 +78,7 @@ typedef enum {
   /* returned by the call itself; nothing was enqueued */
   OXA_ERR_NULL = 1,          /* a required pointer is NULL */
   OXA_ERR_UNSUPPORTED = 2,   /* head_dim != 128, page_size != 16, unknown layout */
-  OXA_ERR_SHAPE = 3,         /* a count is out of range, or Hq % Hkv != 0 */
+  OXA_ERR_SHAPE = 3,         /* a count or scalar is out of range, or Hq % Hkv != 0 */
   OXA_ERR_ALIGN = 4,         /* a bf16 tensor or the workspace is not 16-byte aligned */
   OXA_ERR_ALIAS = 5,         /* an output region overlaps an input or another output */
   OXA_ERR_WORKSPACE = 6,     /* workspace NULL or smaller than the size query returns */

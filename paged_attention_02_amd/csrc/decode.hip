@@ -9,18 +9,22 @@
 // F32 softmax state) and section "Domain coverage" (NHD and HND paged decode).
 //
 // Work decomposition (this design, not the pages'): one work-group per
-// (partition, kv head, q-head tile of up to 32 heads, sequence).  Each wave of
-// the group walks 32-token blocks (two pages) of the partition and keeps its
-// own online-softmax state; the waves are merged through LDS at the end.
+// (partition, kv head, tile of up to 16 grouped q heads, sequence), four
+// waves each.  A group of more than 16 q heads is served by several
+// work-groups that read the same K/V; they are placed on the same XCD (work
+// groups are handed to the 8 XCDs round-robin by linear id), so the repeat
+// read is an L2 hit rather than HBM traffic.  Each wave walks 32-token
+// blocks (two pages) of the partition with its own online-softmax state; the
+// waves merge through LDS at the end.
 //
-// Per 32-token block a wave computes S^T = K * Q^T with eight
-// v_mfma_f32_32x32x16_bf16 (tokens are the M dimension, the grouped q heads of
-// one kv head are N), so every lane's K operand is one contiguous 128-byte run
-// of a K row, read straight from HBM into registers.  The result leaves each
-// lane with one q head and 16 tokens, so the softmax max needs only an
-// in-register reduction and one cross-half lane swap.  The probabilities are
-// already in the B-operand layout of the PV product O^T = V^T * P^T; V^T comes
-// from the block's V rows staged in LDS through the transpose read.
+// Per block a wave loads K and V rows with whole-cache-line loads (16 lanes
+// per 256-byte row) into registers while the previous block is computed from
+// LDS, then stages them into its LDS slice (XOR-swizzled rows).  S^T = K Q^T
+// takes 8 v_mfma_f32_16x16x32_bf16 (tokens are M, the q heads N); each lane
+// then holds one head and 8 tokens, so the softmax max is an in-register
+// reduction plus two lane exchanges, and the probabilities already form the
+// B operand of O^T = V^T P^T (8 more MFMAs, V^T through the LDS transpose
+// read).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -31,7 +35,10 @@ constexpr int kStatusPageRange = 16;
 constexpr int kStatusIndptr = 17;
 constexpr int kStatusSeqLen = 18;
 
-constexpr int kVRow = kHeadDim + 8;  // staged V row stride in bf16 (16-byte pad)
+constexpr int kNW = 4;                 // waves per work-group
+constexpr int kHT = 16;                // q heads per work-group (MFMA N)
+constexpr int kPidWin = 1024;          // page ids of a partition staged in LDS per window
+constexpr int kStageBytes = 32 * 256;  // one 32-token block of K (or V) rows
 
 struct DecodeParams {
   const uint16_t* q;
@@ -47,27 +54,59 @@ struct DecodeParams {
   float* ws_lse;
   int32_t batch, hq, hkv, group, head_tiles;
   int32_t num_pages, num_page_entries, max_seq_len, num_partitions, chunk_pages;
+  int32_t num_items;  // batch * hkv * num_partitions
   float scale_log2;
 };
 
-template <int LAYOUT>
-__device__ __forceinline__ int64_t kv_row(int64_t pid, int slot, int h, int hkv) {
-  if (LAYOUT == 0) return ((pid * kPage + slot) * hkv + h) * kHeadDim;  // NHD
-  return ((pid * hkv + h) * kPage + slot) * kHeadDim;                   // HND
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-template <int LAYOUT, int NW>
-__global__ __launch_bounds__(NW * 64) void paged_decode_kernel(DecodeParams p) {
+// LDS byte offset of 16-byte chunk `c` of row `row` in a tile of 256-byte rows,
+// chunks XOR-swizzled by 2*(row % 8) + (row / 8) % 2.  Conflict-free for the
+// three access patterns used here: 16 lanes writing one row's 16 chunks;
+// 16 lanes reading one chunk of 16 consecutive rows (the K operand); and the
+// 16x16x32 transpose read, where 32 lanes read 8 consecutive rows x 32 bytes.
+__device__ __forceinline__ int swz16(int row, int c) {
+  const int sw = ((row & 7) << 1) | ((row >> 3) & 1);
+  return row * 256 + ((c ^ sw) << 4);
+}
+
+__device__ __forceinline__ float xor16_max(float v) { return fmaxf(v, __shfl_xor(v, 16)); }
+__device__ __forceinline__ float xor16_sum(float v) { return v + __shfl_xor(v, 16); }
+
+struct BlockLoad {
+  u32x4_t k[8];
+  u32x4_t v[8];
+};
+
+template <int LAYOUT>
+__global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void paged_decode_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y / p.head_tiles;
-  const int ht = blockIdx.y - kvh * p.head_tiles;
-  const int b = blockIdx.z;
+  // Work-group -> work item.  Linear ids go to XCDs round-robin (id % 8), so
+  // the head tiles of one (partition, sequence, kv head) share an XCD.
+  const int id = blockIdx.x;
+  const int xcd = id & 7;
+  const int rest = id >> 3;
+  const int ht = rest % p.head_tiles;
+  const int item = (rest / p.head_tiles) * 8 + xcd;
+  if (item >= p.num_items) return;  // padding of the XCD mapping
+  // Items are numbered (partition, sequence, kv head) with the partition
+  // slowest, so each XCD receives an even share of every partition index
+  // (later partitions of short sequences are empty).
+  const int kvh = item % p.hkv;
+  const int b = (item / p.hkv) % p.batch;
+  const int part = item / (p.hkv * p.batch);
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 31;   // MFMA N index: q head within the tile
-  const int gi = lane >> 5;    // which half of the k slots this lane holds
+  const int col = lane & 15;  // MFMA N index: q head within the tile
+  const int gq = lane >> 4;   // which quarter of the k slots this lane holds
 
   // ---- sequence metadata (uniform) --------------------------------------
   const int L = p.seq_lens[b];
@@ -78,7 +117,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(DecodeParams p) {
                       (int64_t)(hi - lo) * kPage >= (int64_t)L;
   const bool seq_ok = len_ok && ptr_ok;
 
-  if (p.status != nullptr && part == 0 && blockIdx.y == 0) {
+  if (p.status != nullptr && part == 0 && kvh == 0 && ht == 0) {
     int code = 0;
     if (!len_ok) {
       code = kStatusSeqLen;
@@ -87,7 +126,7 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(DecodeParams p) {
     } else {
       const int need = (L + kPage - 1) / kPage;
       int bad = 0;
-      for (int i = tid; i < need; i += NW * 64) {
+      for (int i = tid; i < need; i += kNW * 64) {
         const int pid = p.page_indices[lo + i];
         bad |= (pid < 0 || pid >= p.num_pages);
       }
@@ -99,152 +138,226 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(DecodeParams p) {
   const int chunk_tokens = p.chunk_pages * kPage;
   const int t0 = part * chunk_tokens;
   const int t1 = seq_ok ? min(t0 + chunk_tokens, L) : t0;
-  const int nblk = t1 > t0 ? (t1 - t0 + 31) / 32 : 0;
+  const int npages = t1 > t0 ? (t1 - t0 + kPage - 1) / kPage : 0;
 
-  // ---- Q^T fragments (B operand), loaded once ---------------------------
-  const int ncol = min(32, p.group - ht * 32);  // real q heads in this tile
+  // ---- Q^T fragments (B operand), loaded once: lane l holds head l%16,
+  // dims 32*kk + 8*(l/16) .. +8 for k-step kk
+  const int ncol = min(kHT, p.group - ht * kHT);  // real q heads in this tile
   const bool col_ok = col < ncol;
-  const int head = kvh * p.group + ht * 32 + col;
-  u32x4_t qf[8];
+  const int head = kvh * p.group + ht * kHT + col;
+  u32x4_t qf[4];
   if (col_ok) {
-    const uint16_t* qp = p.q + ((int64_t)b * p.hq + head) * kHeadDim + gi * 64;
+    const uint16_t* qp = p.q + ((int64_t)b * p.hq + head) * kHeadDim + 8 * gq;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = ldg16(qp + 8 * s);
+    for (int kk = 0; kk < 4; ++kk) qf[kk] = ldg16(qp + 32 * kk);
   } else {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = u32x4_t{0, 0, 0, 0};
+    for (int kk = 0; kk < 4; ++kk) qf[kk] = u32x4_t{0, 0, 0, 0};
   }
 
-  f32x16_t acc[4];
+  f32x4_t acc[8];  // O^T: d-block j holds dims 16j + 4*(l/16) + i for head l%16
 #pragma unroll
-  for (int d = 0; d < 4; ++d) acc[d] = f32x16_t{};
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY;
   float lsum = 0.f;
 
-  uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * 32 * kVRow;
-  const int g16 = (lane >> 4) & 1;  // 16-lane group parity: which 16 columns of a 32-wide d block
+  int* pids = reinterpret_cast<int*>(smem);                         // [kPidWin]
+  unsigned char* ks = smem + kPidWin * 4 + wave * 2 * kStageBytes;  // K rows
+  unsigned char* vs = ks + kStageBytes;                             // V rows
   const int i16 = lane & 15;
+  const uint16_t* kbase = p.kp + (int64_t)kvh * (LAYOUT == 0 ? kHeadDim : kPage * kHeadDim);
+  const uint16_t* vbase = p.vp + (int64_t)kvh * (LAYOUT == 0 ? kHeadDim : kPage * kHeadDim);
+  // elements between consecutive slots of one kv head inside a page
+  const int row_stride = LAYOUT == 0 ? p.hkv * kHeadDim : kHeadDim;
+  const int64_t page_elems = (int64_t)kPage * p.hkv * kHeadDim;
+  const int64_t lane_off = (int64_t)(lane >> 4) * row_stride + 8 * (lane & 15);
 
-  for (int blk = wave; blk < nblk; blk += NW) {
-    const int tb = t0 + blk * 32;  // first token of the block (page aligned)
-    const int lp = lo + tb / kPage;
-    const int pidA = p.page_indices[lp];
-    const int pidB = (tb + kPage < t1) ? p.page_indices[lp + 1] : -1;
-    const bool okA = pidA >= 0 && pidA < p.num_pages;
-    const bool okB = (tb + kPage < t1) && pidB >= 0 && pidB < p.num_pages;
-
-    // this lane's load token: block row `col`
-    const bool ld_ok = (tb + col < t1) && (col < kPage ? okA : okB);
-    u32x4_t kf[8], vf[8];
-    if (ld_ok) {
-      const int pid = col < kPage ? pidA : pidB;
-      const int64_t row = kv_row<LAYOUT>(pid, col & (kPage - 1), kvh, p.hkv) + gi * 64;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) kf[s] = ldg16(p.kp + row + 8 * s);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) vf[s] = ldg16(p.vp + row + 8 * s);
-    } else {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) { kf[s] = u32x4_t{0, 0, 0, 0}; vf[s] = u32x4_t{0, 0, 0, 0}; }
+  for (int w0 = 0; w0 < npages; w0 += kPidWin) {
+    const int wpages = min(kPidWin, npages - w0);
+    __syncthreads();
+    for (int i = tid; i < ((wpages + 1) & ~1); i += kNW * 64) {  // even count: blocks read pairs
+      const int pid = i < wpages ? p.page_indices[lo + t0 / kPage + w0 + i] : -1;
+      pids[i] = (pid >= 0 && pid < p.num_pages) ? pid : -1;
     }
+    __syncthreads();
+    const int tw = t0 + w0 * kPage;                 // first token of the window
+    const int tw1 = min(t1, tw + kPidWin * kPage);  // end of the window
+    const int nb = (tw1 - tw + 31) / 32;
 
-    // S^T[token][head] over the 128-wide head dim: 8 k-steps of 16
-    f32x16_t s = f32x16_t{};
+    // Issue the K/V loads of window block `blk`: load s brings rows 4s .. 4s+3
+    // of the 32-token block, 16 lanes per 256-byte row.  Unconditional loads
+    // (straight-line code keeps the wait counters exact): a missing or invalid
+    // page reads page 0 and those rows are discarded; a block past the
+    // window's end re-reads its last block (a cache hit, never used).
+    auto issue = [&](int blk, BlockLoad& bl) {
+      const int bi = min(blk, nb - 1);
+      const int pa = max(pids[2 * bi], 0);
+      const int pb = max(pids[2 * bi + 1], 0);
+      const uint16_t* ka = kbase + pa * page_elems + lane_off;
+      const uint16_t* kb = kbase + pb * page_elems + lane_off;
+      const uint16_t* va = vbase + pa * page_elems + lane_off;
+      const uint16_t* vb = vbase + pb * page_elems + lane_off;
 #pragma unroll
-    for (int st = 0; st < 8; ++st) s = mfma_32x32x16(kf[st], qf[st], s);
-
-    // stage V rows (zeros for tokens that do not exist) for the transpose read
-#pragma unroll
-    for (int st = 0; st < 8; ++st)
-      *reinterpret_cast<u32x4_t*>(vs + col * kVRow + gi * 64 + 8 * st) = vf[st];
-
-    // mask, scale into the log2 domain, online softmax update
-    float sv[16];
-    float mblk = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = 8 * (r >> 2) + 4 * gi + (r & 3);
-      const bool ok = (tb + t < t1) && (t < kPage ? okA : okB);
-      sv[r] = ok ? s[r] * p.scale_log2 : -INFINITY;
-      mblk = fmaxf(mblk, sv[r]);
-    }
-    mblk = pair_max32(mblk);
-    const float mnew = fmaxf(m, mblk);
-    const float muse = mnew == -INFINITY ? 0.f : mnew;
-    const float corr = exp2f(m - muse);
-    float psum = 0.f;
-    uint32_t pk[8];
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = exp2f(sv[r] - muse);
-      const float p1 = exp2f(sv[r + 1] - muse);
-      psum += p0 + p1;
-      pk[r >> 1] = pack_bf16x2(p0, p1);
-    }
-    lsum = lsum * corr + psum;
-    m = mnew;
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[d][r] *= corr;
-
-    // O^T[d][head] += V^T[d][token] * P^T[token][head], 2 k-steps x 4 d-blocks
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const u32x4_t pf = u32x4_t{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
-      const uint16_t* vrow = vs + (16 * ks + 4 * gi + (i16 >> 2)) * kVRow + 16 * g16 + 4 * (i16 & 3);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const u32x2_t a0 = lds_read_tr16(vrow + 32 * d);
-        const u32x2_t a1 = lds_read_tr16(vrow + 8 * kVRow + 32 * d);
-        acc[d] = mfma_32x32x16(u32x4_t{a0[0], a0[1], a1[0], a1[1]}, pf, acc[d]);
+      for (int s = 0; s < 4; ++s) {
+        bl.k[s] = ldg16(ka + 4 * s * row_stride);
+        bl.v[s] = ldg16(va + 4 * s * row_stride);
       }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bl.k[4 + s] = ldg16(kb + 4 * s * row_stride);
+        bl.v[4 + s] = ldg16(vb + 4 * s * row_stride);
+      }
+    };
+
+    // Write a loaded block into this wave's LDS rows; V rows of tokens that
+    // do not exist become zeros (their K rows are masked in `compute`).
+    auto stage = [&](int blk, const BlockLoad& bl) {
+      const int tb = tw + blk * 32;
+      const bool okA = pids[2 * blk] >= 0;
+      const bool okB = (tb + kPage < tw1) && pids[2 * blk + 1] >= 0;
+      const bool full = (tb + 32 <= tw1) && okA && okB;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const int r = 4 * st + (lane >> 4);
+        const int off = swz16(r, lane & 15);
+        *reinterpret_cast<u32x4_t*>(ks + off) = bl.k[st];
+        const bool ok = full || ((tb + r < tw1) && (st < 4 ? okA : okB));
+        *reinterpret_cast<u32x4_t*>(vs + off) = ok ? bl.v[st] : u32x4_t{0, 0, 0, 0};
+      }
+    };
+
+    // Attention over the block staged in LDS.
+    auto compute = [&](int blk) {
+      const int tb = tw + blk * 32;
+      const bool okA = pids[2 * blk] >= 0;
+      const bool okB = (tb + kPage < tw1) && pids[2 * blk + 1] >= 0;
+      const bool full = (tb + 32 <= tw1) && okA && okB;  // wave-uniform
+      // S^T[token][head] for tokens 16*mb .. +15: A operand of lane l is row
+      // 16*mb + l%16, dims 32*kk + 8*(l/16) .. +8
+      f32x4_t s[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        s[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          s[mb] = mfma_16x16x32(
+              *reinterpret_cast<const u32x4_t*>(ks + swz16(16 * mb + i16, 4 * kk + gq)), qf[kk],
+              s[mb]);
+      }
+      // this lane's tokens: 16*mb + 4*gq + i; raw-score max (scale >= 0)
+      float mraw = -INFINITY;
+      if (full) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mraw = fmaxf(mraw, s[mb][i]);
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = 16 * mb + 4 * gq + i;
+            const bool ok = (tb + t < tw1) && (mb == 0 ? okA : okB);
+            s[mb][i] = ok ? s[mb][i] : -INFINITY;
+            mraw = fmaxf(mraw, s[mb][i]);
+          }
+      }
+      const float mblk = pair_max32(xor16_max(mraw)) * p.scale_log2;
+      // Lazy rescaling: exponentials are taken against a reference max that
+      // only moves when a score exceeds it by more than 2^8, so probabilities
+      // stay <= 256 and the accumulator is rescaled rarely.  The result is
+      // the same softmax (the reference cancels in o = acc / l).
+      if (__builtin_amdgcn_ballot_w64(mblk > m + 8.f) != 0) {
+        const float mnew = mblk > m + 8.f ? mblk : m;
+        const float corr = fast_exp2(m - mnew);  // 0 while m is still -inf
+        lsum *= corr;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] *= corr;
+        m = mnew;
+      }
+      const float muse = m == -INFINITY ? 0.f : m;
+      float pv[8];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[4 * mb + i] = fast_exp2(fmaf(s[mb][i], p.scale_log2, -muse));
+      lsum += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+      // P^T B operand: k slot j of lane l is token (j < 4 ? 4gq + j : 16 + 4gq + j - 4)
+      const u32x4_t pf = u32x4_t{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                 pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
+      // O^T[d][head] += V^T[d][token] P^T[token][head] for 8 d-blocks of 16;
+      // V^T through the transpose read: lanes 4e..4e+3 of each 16-lane group
+      // address row (4*gq + e) (then 16 + ...) and 16 dims of d-block j
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = 2 * j + ((i16 & 3) >> 1);
+        const int b8 = 8 * (i16 & 1);
+        const int r = 4 * gq + (i16 >> 2);
+        const u32x2_t a0 = lds_read_tr16(reinterpret_cast<const uint16_t*>(vs + swz16(r, c) + b8));
+        const u32x2_t a1 = lds_read_tr16(reinterpret_cast<const uint16_t*>(vs + swz16(r + 16, c) + b8));
+        acc[j] = mfma_16x16x32(u32x4_t{a0[0], a0[1], a1[0], a1[1]}, pf, acc[j]);
+      }
+    };
+
+    // One register set holds the next block's loads while the current one is
+    // computed from LDS; the loaded block is staged at the end of the step.
+    BlockLoad bl;
+    int blk = wave;
+    if (blk < nb) {
+      issue(blk, bl);
+      stage(blk, bl);
+    }
+    while (blk < nb) {
+      const int nxt = blk + kNW;
+      issue(nxt, bl);
+      compute(blk);
+      if (nxt < nb) stage(nxt, bl);
+      blk = nxt;
     }
   }
 
   // ---- merge the waves' states through LDS -------------------------------
-  lsum = pair_sum32(lsum);
+  lsum = pair_sum32(xor16_sum(lsum));
   __syncthreads();  // staging area is reused below
-  float* red_m = reinterpret_cast<float*>(smem);         // [NW][32]
-  float* red_l = red_m + NW * 32;                         // [NW][32]
-  float* red_o = red_l + NW * 32;                         // [NW][128][ncol]
-  if (gi == 0) {
-    red_m[wave * 32 + col] = m;
-    red_l[wave * 32 + col] = lsum;
+  float* red_m = reinterpret_cast<float*>(smem);  // [kNW][16]
+  float* red_l = red_m + kNW * kHT;               // [kNW][16]
+  float* col_m = red_l + kNW * kHT;               // [16]
+  float* col_l = col_m + kHT;                     // [16]
+  float* red_o = col_l + kHT;                     // [kNW][128][16]
+  if (gq == 0) {
+    red_m[wave * kHT + col] = m;
+    red_l[wave * kHT + col] = lsum;
   }
   __syncthreads();
   float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[w * 32 + col]);
+  for (int w = 0; w < kNW; ++w) M = fmaxf(M, red_m[w * kHT + col]);
   const float Muse = M == -INFINITY ? 0.f : M;
-  const float f = exp2f(m - Muse);
-  if (col_ok) {
+  float Ltot = 0.f;
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int dd = 32 * d + 8 * (r >> 2) + 4 * gi + (r & 3);
-        red_o[(wave * kHeadDim + dd) * ncol + col] = acc[d][r] * f;
-      }
+  for (int w = 0; w < kNW; ++w) Ltot += red_l[w * kHT + col] * fast_exp2(red_m[w * kHT + col] - Muse);
+  // this wave's share, already normalised by the total softmax sum
+  const float f = Ltot > 0.f ? fast_exp2(m - Muse) / Ltot : 0.f;
+  if (wave == 0 && gq == 0) {
+    col_m[col] = M;
+    col_l[col] = Ltot;
   }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      red_o[(wave * kHeadDim + 16 * j + 4 * gq + i) * kHT + col] = acc[j][i] * f;
   __syncthreads();
   const bool split = p.num_partitions > 1;
-  for (int idx = tid; idx < ncol * kHeadDim; idx += NW * 64) {
+  for (int idx = tid; idx < ncol * kHeadDim; idx += kNW * 64) {
     const int c = idx % ncol;
     const int dd = idx / ncol;
-    float mc = -INFINITY;
+    float val = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) mc = fmaxf(mc, red_m[w * 32 + c]);
-    const float mcu = mc == -INFINITY ? 0.f : mc;
-    float lc = 0.f, oc = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      lc += red_l[w * 32 + c] * exp2f(red_m[w * 32 + c] - mcu);
-      oc += red_o[(w * kHeadDim + dd) * ncol + c];
-    }
-    const float val = lc > 0.f ? oc / lc : 0.f;
-    const float lse_val = lc > 0.f ? (mc + __log2f(lc)) * kLn2 : -INFINITY;
-    const int64_t hrow = (int64_t)b * p.hq + kvh * p.group + ht * 32 + c;
+    for (int w = 0; w < kNW; ++w) val += red_o[(w * kHeadDim + dd) * kHT + c];
+    const float lc = col_l[c];
+    const float lse_val = lc > 0.f ? (col_m[c] + __log2f(lc)) * kLn2 : -INFINITY;
+    const int64_t hrow = (int64_t)b * p.hq + kvh * p.group + ht * kHT + c;
     if (split) {
       const int64_t prow = hrow * p.num_partitions + part;
       p.ws_o[prow * kHeadDim + dd] = val;
@@ -256,36 +369,55 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_kernel(DecodeParams p) {
   }
 }
 
-// LSE merge of split-K partial states: one 128-thread group per (sequence, q head).
+// LSE merge of split-K partial states: one 128-thread group per (sequence,
+// q head), thread d owns output dim d.  One pass with a running maximum over
+// chunks of 8 partitions, whose loads are issued together.
 __global__ __launch_bounds__(128) void merge_partials_kernel(const float* ws_o, const float* ws_lse,
                                                              int num_partitions, uint16_t* o,
                                                              float* lse) {
+  constexpr int kChunk = 8;
   const int64_t row = blockIdx.x;
   const int d = threadIdx.x;
   const float* lp = ws_lse + row * num_partitions;
-  const float* op = ws_o + row * num_partitions * kHeadDim;
-  float mx = -INFINITY;
-  for (int i = 0; i < num_partitions; ++i) mx = fmaxf(mx, lp[i]);
-  const float mu = mx == -INFINITY ? 0.f : mx;
-  float wsum = 0.f, acc = 0.f;
-  for (int i = 0; i < num_partitions; ++i) {
-    const float w = __expf(lp[i] - mu);
-    wsum += w;
-    acc += w * op[(int64_t)i * kHeadDim + d];
+  const float* op = ws_o + row * num_partitions * kHeadDim + d;
+  float mx = -INFINITY, wsum = 0.f, acc = 0.f;
+  for (int i0 = 0; i0 < num_partitions; i0 += kChunk) {
+    float w[kChunk], v[kChunk];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      const bool in = i0 + j < num_partitions;
+      w[j] = in ? lp[i0 + j] : -INFINITY;
+      v[j] = in ? op[(int64_t)(i0 + j) * kHeadDim] : 0.f;
+    }
+    float cm = mx;
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) cm = fmaxf(cm, w[j]);
+    if (cm == -INFINITY) continue;  // nothing live yet
+    const float r = __expf(mx - cm);  // 0 while mx is -inf
+    wsum *= r;
+    acc *= r;
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      const float e = __expf(w[j] - cm);
+      wsum += e;
+      acc += e * v[j];
+    }
+    mx = cm;
   }
   const float val = wsum > 0.f ? acc / wsum : 0.f;
   o[row * kHeadDim + d] = (uint16_t)(pack_bf16x2(val, 0.f) & 0xffffu);
   if (d == 0 && lse != nullptr) lse[row] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
 }
 
-template <int LAYOUT, int NW>
+template <int LAYOUT>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
-  const int ncol = p.group < 32 ? p.group : 32;
-  const size_t stage = (size_t)NW * 32 * kVRow * sizeof(uint16_t);
-  const size_t reduce = (size_t)NW * 64 * sizeof(float) + (size_t)NW * kHeadDim * ncol * sizeof(float);
+  const size_t stage = (size_t)kPidWin * 4 + (size_t)kNW * 2 * kStageBytes;
+  const size_t reduce = ((size_t)kNW * 2 * kHT + 2 * kHT) * sizeof(float) +
+                        (size_t)kNW * kHeadDim * kHT * sizeof(float);
   const size_t lds = stage > reduce ? stage : reduce;
-  dim3 grid(p.num_partitions, p.hkv * p.head_tiles, p.batch);
-  hipLaunchKernelGGL((paged_decode_kernel<LAYOUT, NW>), grid, dim3(NW * 64), lds, stream, p);
+  const int64_t groups = ((int64_t)(p.num_items + 7) / 8) * 8 * p.head_tiles;
+  hipLaunchKernelGGL((paged_decode_kernel<LAYOUT>), dim3((unsigned)groups), dim3(kNW * 64), lds,
+                     stream, p);
   return hipGetLastError();
 }
 
@@ -308,18 +440,15 @@ hipError_t launch_paged_decode(const DecodeLaunch& a, hipStream_t stream) {
   p.hq = a.hq;
   p.hkv = a.hkv;
   p.group = a.hq / a.hkv;
-  p.head_tiles = (p.group + 31) / 32;
+  p.head_tiles = (p.group + kHT - 1) / kHT;
   p.num_pages = a.num_pages;
   p.num_page_entries = a.num_page_entries;
   p.max_seq_len = a.max_seq_len;
   p.num_partitions = a.num_partitions;
   p.chunk_pages = a.chunk_pages;
+  p.num_items = a.batch * a.hkv * a.num_partitions;
   p.scale_log2 = a.sm_scale * kLog2e;
-  hipError_t e;
-  if (a.layout == 0)
-    e = launch_decode_t<0, 8>(p, stream);
-  else
-    e = launch_decode_t<1, 8>(p, stream);
+  hipError_t e = a.layout == 0 ? launch_decode_t<0>(p, stream) : launch_decode_t<1>(p, stream);
   if (e != hipSuccess || a.num_partitions == 1) return e;
   hipLaunchKernelGGL(merge_partials_kernel, dim3(a.batch * a.hq), dim3(kHeadDim), 0, stream,
                      a.ws_o, a.ws_lse, a.num_partitions, a.o, a.lse);

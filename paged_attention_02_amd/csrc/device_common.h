@@ -83,6 +83,21 @@ __host__ __device__ __forceinline__ uint16_t bf16_from_double_rne(double x) {
   return (uint16_t)(sign | bits);
 }
 
+// 2^x on the transcendental unit (v_exp_f32; results below 2^-126 flush to
+// zero, which a softmax weight may do)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Byte offset of 16-byte chunk `c` of row `row` in an LDS tile of 256-byte
+// rows (128 bf16) whose chunks are XOR-swizzled by 4*(row % 4) + (row / 4) % 4.
+// With this swizzle three access patterns are free of bank conflicts:
+// 16 lanes writing the 16 chunks of one row, lanes reading one chunk of 16
+// consecutive rows (the K operand), and the transpose read of 4 consecutive
+// rows x 64 bytes (the V operand).
+__device__ __forceinline__ int swz_off(int row, int c) {
+  const int sw = ((row & 3) << 2) | ((row >> 2) & 3);
+  return row * 256 + ((c ^ sw) << 4);
+}
+
 // max of v over the lane pair (l, l ^ 32)
 __device__ __forceinline__ float pair_max32(float v) {
   const uint32_t b = __float_as_uint(v);

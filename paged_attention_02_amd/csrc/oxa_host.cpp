@@ -188,11 +188,12 @@ oxa_status oxa_paged_decode(hipStream_t stream, const uint16_t* q, int32_t batch
   if (oxa_status s = check_heads(num_qo_heads, num_kv_heads, head_dim)) return s;
   if (oxa_status s = check_paging(page_size, layout, num_pages, num_page_entries)) return s;
   if (batch < 1 || batch > kMaxGridYZ || max_seq_len < 1 || num_partitions < 1 ||
-      num_partitions > 1024 || !std::isfinite(sm_scale))
+      num_partitions > 1024 || !(sm_scale >= 0.f) || !std::isfinite(sm_scale))
     return OXA_ERR_SHAPE;
-  const int32_t group = num_qo_heads / num_kv_heads;
-  if ((uint64_t)num_kv_heads * (uint64_t)((group + 31) / 32) > (uint64_t)kMaxGridYZ)
-    return OXA_ERR_SHAPE;
+  // one work-group per (sequence, kv head, partition, 16-head tile), padded to 8
+  const uint64_t group = (uint64_t)(num_qo_heads / num_kv_heads);
+  const uint64_t items = (uint64_t)batch * num_kv_heads * num_partitions;
+  if (((items + 7) / 8) * 8 * ((group + 15) / 16) > 0x7fffffffull) return OXA_ERR_SHAPE;
   if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(o, 16) ||
       !aligned(workspace, 16) || !aligned(lse, 4) || !aligned(status, 4) ||
       !aligned(page_indptr, 4) || !aligned(page_indices, 4) || !aligned(seq_lens, 4))
@@ -272,7 +273,7 @@ oxa_status oxa_ragged_prefill(hipStream_t stream, const uint16_t* q, const uint1
   if (!q || !k || !v || !qo_indptr || !kv_indptr || !o) return OXA_ERR_NULL;
   if (oxa_status s = check_heads(num_qo_heads, num_kv_heads, head_dim)) return s;
   if (batch < 1 || batch > kMaxGridYZ || nnz_qo < 0 || nnz_kv < 0 || max_qo_len < 1 ||
-      max_kv_len < 1 || !std::isfinite(sm_scale))
+      max_kv_len < 1 || !(sm_scale >= 0.f) || !std::isfinite(sm_scale))
     return OXA_ERR_SHAPE;
   const int32_t group = num_qo_heads / num_kv_heads;
   if (prefill_tiles(num_qo_heads, num_kv_heads, max_qo_len) > (uint64_t)kMaxGridYZ ||
@@ -332,7 +333,7 @@ oxa_status oxa_paged_prefill(hipStream_t stream, const uint16_t* q, const int32_
   if (oxa_status s = check_heads(num_qo_heads, num_kv_heads, head_dim)) return s;
   if (oxa_status s = check_paging(page_size, layout, num_pages, num_page_entries)) return s;
   if (batch < 1 || batch > kMaxGridYZ || nnz_qo < 0 || max_qo_len < 1 || max_seq_len < 1 ||
-      !std::isfinite(sm_scale))
+      !(sm_scale >= 0.f) || !std::isfinite(sm_scale))
     return OXA_ERR_SHAPE;
   const int32_t group = num_qo_heads / num_kv_heads;
   if (prefill_tiles(num_qo_heads, num_kv_heads, max_qo_len) > (uint64_t)kMaxGridYZ ||

@@ -92,53 +92,58 @@ __device__ __forceinline__ SeqInfo seq_info(const PrefillParams& p, int b) {
   return s;
 }
 
+constexpr int kPidWin = 2048;  // page ids staged in LDS per window (paged K/V)
+
+// Issue the loads of K/V tile `kt` (64 keys): thread tid brings the 16-byte
+// chunk `tid % 16` of rows tid/16 and tid/16 + 32, so 16 lanes read one whole
+// 256-byte row.  Loads are unconditional - straight-line code keeps the wait
+// counters exact - and rows that do not exist read a valid stand-in (key 0 of
+// the sequence, or page 0); `ok` marks the real rows for store_tile.
 template <bool PAGED, int LAYOUT>
 __device__ __forceinline__ void load_tile(const PrefillParams& p, const SeqInfo& si, int kvh,
-                                          int kt, int tid, u32x4_t* kr, u32x4_t* vr) {
+                                          int kt, int tid, const int* pids, int wbase,
+                                          u32x4_t* kr, u32x4_t* vr, bool* ok) {
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int c = tid + u * (kNW * 64);
     const int row = c >> 4;
     const int piece = c & 15;
     const int key = kt * kBN + row;
-    bool ok = key < si.klen;
-    int64_t off = 0;
-    if (ok) {
-      if (!PAGED) {
-        off = ((int64_t)(si.kbase + key) * p.hkv + kvh) * kHeadDim;
-      } else {
-        const int pid = p.page_indices[si.kbase + key / kPage];
-        ok = pid >= 0 && pid < p.num_pages;
-        const int slot = key & (kPage - 1);
-        off = LAYOUT == 0 ? (((int64_t)pid * kPage + slot) * p.hkv + kvh) * kHeadDim
-                          : (((int64_t)pid * p.hkv + kvh) * kPage + slot) * kHeadDim;
-      }
-    }
-    if (ok) {
-      kr[u] = ldg16(p.k + off + piece * 8);
-      vr[u] = ldg16(p.v + off + piece * 8);
+    int64_t off;
+    if (!PAGED) {
+      ok[u] = key < si.klen;
+      const int kc = ok[u] ? key : 0;
+      off = ((int64_t)(si.kbase + kc) * p.hkv + kvh) * kHeadDim;
     } else {
-      kr[u] = u32x4_t{0, 0, 0, 0};
-      vr[u] = u32x4_t{0, 0, 0, 0};
+      const int pid = key < si.klen ? pids[key / kPage - wbase] : -1;
+      ok[u] = pid >= 0;
+      const int pc = ok[u] ? pid : 0;
+      const int slot = key & (kPage - 1);
+      off = LAYOUT == 0 ? (((int64_t)pc * kPage + slot) * p.hkv + kvh) * kHeadDim
+                        : (((int64_t)pc * p.hkv + kvh) * kPage + slot) * kHeadDim;
     }
+    kr[u] = ldg16(p.k + off + piece * 8);
+    vr[u] = ldg16(p.v + off + piece * 8);
   }
 }
 
 __device__ __forceinline__ void store_tile(uint16_t* ks, uint16_t* vs, int tid, const u32x4_t* kr,
-                                           const u32x4_t* vr) {
+                                           const u32x4_t* vr, const bool* ok) {
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int c = tid + u * (kNW * 64);
     const int row = c >> 4;
     const int piece = c & 15;
-    *reinterpret_cast<u32x4_t*>(ks + row * kRow + piece * 8) = kr[u];
-    *reinterpret_cast<u32x4_t*>(vs + row * kRow + piece * 8) = vr[u];
+    const u32x4_t z = u32x4_t{0, 0, 0, 0};
+    *reinterpret_cast<u32x4_t*>(ks + row * kRow + piece * 8) = ok[u] ? kr[u] : z;
+    *reinterpret_cast<u32x4_t*>(vs + row * kRow + piece * 8) = ok[u] ? vr[u] : z;
   }
 }
 
 template <bool PAGED, int LAYOUT>
 __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
   __shared__ __align__(16) uint16_t smem[4 * kTileElems];  // K0, V0, K1, V1
+  __shared__ int pids[PAGED ? kPidWin : 1];
   const int kvh = blockIdx.x / p.head_tiles;
   const int ht = blockIdx.x - kvh * p.head_tiles;
   const int b = blockIdx.y;
@@ -201,17 +206,45 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
   // smallest visible-key limit among the work-group's rows: tiles past it need masks
   const int wg_min_lim = r0 + offset;
 
+  // Paged K/V: the sequence's page ids for keys [0, kv_end), staged per window
+  // of kPidWin pages (invalid ids become -1).
+  const int npages_need = (kv_end + kPage - 1) / kPage;
+  auto stage_pids = [&](int wbase) {
+    for (int i = tid; i < kPidWin; i += kNW * 64) {
+      const int pg = wbase + i;
+      int v = -1;
+      if (pg < npages_need) {
+        const int pid = p.page_indices[si.kbase + pg];
+        v = (pid >= 0 && pid < p.num_pages) ? pid : -1;
+      }
+      pids[i] = v;
+    }
+  };
+  constexpr int kTilesPerWin = kPidWin * kPage / kBN;
+  int wbase = 0;
+  if (PAGED) stage_pids(0);
+  __syncthreads();
+
   u32x4_t kr[2], vr[2];
+  bool okr[2];
   if (ntiles > 0) {
-    load_tile<PAGED, LAYOUT>(p, si, kvh, 0, tid, kr, vr);
-    store_tile(smem, smem + kTileElems, tid, kr, vr);
+    load_tile<PAGED, LAYOUT>(p, si, kvh, 0, tid, pids, wbase, kr, vr, okr);
+    store_tile(smem, smem + kTileElems, tid, kr, vr, okr);
   }
   __syncthreads();
 
   for (int kt = 0; kt < ntiles; ++kt) {
     const uint16_t* ks = smem + (kt & 1) * 2 * kTileElems;
     const uint16_t* vs = ks + kTileElems;
-    if (kt + 1 < ntiles) load_tile<PAGED, LAYOUT>(p, si, kvh, kt + 1, tid, kr, vr);
+    if (PAGED && kt + 1 < ntiles && (kt + 1) % kTilesPerWin == 0) {
+      // the next tile starts a new page-id window (every waves' reads of the
+      // current window are done: only tile kt+1 uses page ids from here on)
+      wbase = (kt + 1) / kTilesPerWin * kPidWin;
+      __syncthreads();
+      stage_pids(wbase);
+      __syncthreads();
+    }
+    if (kt + 1 < ntiles) load_tile<PAGED, LAYOUT>(p, si, kvh, kt + 1, tid, pids, wbase, kr, vr, okr);
 
     // S^T[key][col] for the 64 keys of the tile: 2 key blocks x 8 k-steps
     f32x16_t s[2];
@@ -251,8 +284,6 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
     mt = pair_max32(mt);
     const float mnew = fmaxf(m, mt);
     const float muse = mnew == -INFINITY ? 0.f : mnew;
-    const float corr = exp2f(m - muse);
-    m = mnew;
     float psum = 0.f;
     uint32_t pk[16];
 #pragma unroll
@@ -264,11 +295,16 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
         psum += p0 + p1;
         pk[mb * 8 + (r >> 1)] = pack_bf16x2(p0, p1);
       }
-    lsum = lsum * corr + psum;
+    if (__builtin_amdgcn_ballot_w64(mnew != m) != 0) {  // rescale only when a max moved
+      const float corr = exp2f(m - muse);
+      lsum *= corr;
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
+      for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[d][r] *= corr;
+        for (int r = 0; r < 16; ++r) acc[d][r] *= corr;
+    }
+    lsum += psum;
+    m = mnew;
 
     // O^T += V^T * P^T over 4 k-steps of 16 keys
 #pragma unroll
@@ -285,7 +321,7 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
 
     if (kt + 1 < ntiles) {
       uint16_t* kn = smem + ((kt + 1) & 1) * 2 * kTileElems;
-      store_tile(kn, kn + kTileElems, tid, kr, vr);
+      store_tile(kn, kn + kTileElems, tid, kr, vr, okr);
     }
     __syncthreads();
   }

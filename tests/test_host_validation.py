@@ -49,6 +49,7 @@ def call_decode(**over):
     (dict(P=1025), oxa.OXA_ERR_SHAPE),
     (dict(num_pages=0), oxa.OXA_ERR_SHAPE),
     (dict(scale=float("nan")), oxa.OXA_ERR_SHAPE),
+    (dict(scale=-0.5), oxa.OXA_ERR_SHAPE),
     (dict(q=addr(0) + 8), oxa.OXA_ERR_ALIGN),
     (dict(seq_lens=addr(5) + 2), oxa.OXA_ERR_ALIGN),
     (dict(P=4), oxa.OXA_ERR_WORKSPACE),
@@ -76,6 +77,7 @@ def call_ragged(**over):
     (dict(hq=8, hkv=3), oxa.OXA_ERR_SHAPE),
     (dict(nnz_qo=-1), oxa.OXA_ERR_SHAPE),
     (dict(max_qo=0), oxa.OXA_ERR_SHAPE),
+    (dict(scale=float("-inf")), oxa.OXA_ERR_SHAPE),
     (dict(max_qo=1 << 30), oxa.OXA_ERR_SHAPE),       # more query tiles than the grid allows
     (dict(v=addr(2) + 4), oxa.OXA_ERR_ALIGN),
     (dict(o=addr(1) + 256), oxa.OXA_ERR_ALIAS),      # o overlaps k
