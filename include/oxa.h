@@ -206,7 +206,9 @@ size_t oxa_paged_decode_workspace_bytes(int32_t batch, int32_t num_qo_heads, int
  * Shapes: q, o [nnz_qo][num_qo_heads][128]; k, v [nnz_kv][num_kv_heads][128];
  * lse [nnz_qo][num_qo_heads] or NULL; qo_indptr, kv_indptr [batch+1].
  * The workspace is reserved (the size query returns 0; pass NULL, 0).
- * Ranges: 1 <= batch, 0 <= nnz_qo, nnz_kv; 1 <= max_qo_len, max_kv_len.
+ * Ranges: 1 <= batch, 0 <= nnz_qo, nnz_kv; 1 <= max_kv_len;
+ * 1 <= max_qo_len <= 4096 * BM, where BM = 256 / min(Hq / Hkv, 256) query
+ * rows form one tile (for example 262144 rows for four q heads per kv head).
  */
 oxa_status oxa_ragged_prefill(
     hipStream_t stream,
@@ -237,6 +239,7 @@ size_t oxa_ragged_prefill_workspace_bytes(int32_t batch, int32_t nnz_qo, int32_t
  * Shapes: q, o [nnz_qo][num_qo_heads][128]; lse [nnz_qo][num_qo_heads] or
  * NULL; qo_indptr, page_indptr [batch+1]; seq_lens [batch].
  * The workspace is reserved (the size query returns 0; pass NULL, 0).
+ * Ranges as for oxa_ragged_prefill, with max_seq_len in place of max_kv_len.
  */
 oxa_status oxa_paged_prefill(
     hipStream_t stream,

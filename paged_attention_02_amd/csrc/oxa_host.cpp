@@ -45,6 +45,7 @@ bool any_alias(const Region* outs, int nout, const Region* ins, int nin) {
 
 constexpr uint64_t kRowBytes = OXA_HEAD_DIM * 2;  // one bf16 head row
 constexpr int kMaxGridYZ = 65535;
+constexpr uint64_t kMaxPrefillTiles = 4096;
 
 oxa_status check_heads(int32_t hq, int32_t hkv, int32_t head_dim) {
   if (head_dim != OXA_HEAD_DIM) return OXA_ERR_UNSUPPORTED;
@@ -250,8 +251,9 @@ size_t oxa_paged_prefill_workspace_bytes(int32_t, int32_t, int32_t, int32_t) { r
 
 namespace {
 
-// Query tiles of the prefill grid for the given head grouping (256 columns
-// per work-group, BM = 256 / min(group, 256) rows each).
+// Query tiles per sequence for the given head grouping (256 columns per
+// work-group, BM = 256 / min(group, 256) rows each).  The prefill schedule
+// orders at most kMaxPrefillTiles tile indices.
 uint64_t prefill_tiles(int32_t hq, int32_t hkv, int32_t max_qo_len) {
   const int32_t group = hq / hkv;
   const int32_t gwg = group < 256 ? group : 256;
@@ -276,7 +278,7 @@ oxa_status oxa_ragged_prefill(hipStream_t stream, const uint16_t* q, const uint1
       max_kv_len < 1 || !(sm_scale >= 0.f) || !std::isfinite(sm_scale))
     return OXA_ERR_SHAPE;
   const int32_t group = num_qo_heads / num_kv_heads;
-  if (prefill_tiles(num_qo_heads, num_kv_heads, max_qo_len) > (uint64_t)kMaxGridYZ ||
+  if (prefill_tiles(num_qo_heads, num_kv_heads, max_qo_len) > kMaxPrefillTiles ||
       (uint64_t)num_kv_heads * (uint64_t)((group + 255) / 256) > 0x7fffffffull)
     return OXA_ERR_SHAPE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
@@ -336,7 +338,7 @@ oxa_status oxa_paged_prefill(hipStream_t stream, const uint16_t* q, const int32_
       !(sm_scale >= 0.f) || !std::isfinite(sm_scale))
     return OXA_ERR_SHAPE;
   const int32_t group = num_qo_heads / num_kv_heads;
-  if (prefill_tiles(num_qo_heads, num_kv_heads, max_qo_len) > (uint64_t)kMaxGridYZ ||
+  if (prefill_tiles(num_qo_heads, num_kv_heads, max_qo_len) > kMaxPrefillTiles ||
       (uint64_t)num_kv_heads * (uint64_t)((group + 255) / 256) > 0x7fffffffull)
     return OXA_ERR_SHAPE;
   if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(o, 16) ||

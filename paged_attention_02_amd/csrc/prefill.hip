@@ -10,15 +10,23 @@
 // Work decomposition (this design): a work-group owns 256 (query row, q head)
 // columns that read the same kv head - BM = 256 / G rows of the G = Hq / Hkv
 // heads of one group - so each K/V tile staged in LDS serves all of them.
-// Eight waves take 32 columns each.  Per 64-key tile a wave forms
-// S^T = K * Q^T (16 x v_mfma_f32_32x32x16_bf16, K from LDS, Q^T resident in
-// registers), masks only where the tile crosses the causal diagonal or the
-// sequence end, updates the f32 online softmax, and accumulates
-// O^T = V^T * P^T (16 more MFMAs; V^T through the LDS transpose read, P^T
-// straight from the score registers).  Tiles are scheduled longest-first:
-// the query-tile index is the slowest grid dimension, counted from the end.
+// Four waves (one per SIMD) take 64 columns each, as two 32-column blocks, so
+// every K or V operand fetched from LDS feeds two matrix-core instructions.
+// Per 64-key tile a wave forms S^T = K * Q^T (32 x v_mfma_f32_32x32x16_bf16,
+// K from LDS, Q^T resident in registers), masks only where the tile crosses
+// the causal diagonal or the sequence end, updates the f32 online softmax
+// (lazy rescaling), and accumulates O^T = V^T * P^T (32 more MFMAs; V^T
+// through the LDS transpose read, P^T straight from the score registers).
+// K/V tiles are double-buffered: the next tile's loads are in flight during
+// the current tile's math.  Tiles are scheduled longest-first: the
+// query-tile index is the slowest grid dimension, counted from the end.
 #include "device_common.h"
 #include "kernels.h"
+
+#ifndef PREFILL_NW
+#define PREFILL_NW 8
+#define PREFILL_CB 1
+#endif
 
 namespace oxa {
 namespace {
@@ -29,10 +37,12 @@ constexpr int kStatusSeqLen = 18;
 constexpr int kStatusCausal = 19;
 
 constexpr int kBN = 64;              // keys per tile
-constexpr int kNW = 8;               // waves per work-group
-constexpr int kCols = kNW * 32;      // (row, head) columns per work-group
-constexpr int kRow = kHeadDim + 8;   // LDS row stride (bf16), 16-byte pad
-constexpr int kTileElems = kBN * kRow;
+constexpr int kNW = PREFILL_NW;      // waves per work-group
+constexpr int kCB = PREFILL_CB;      // 32-column blocks per wave
+constexpr int kLoadIters = kBN * 16 / (kNW * 64);  // 16-byte K (and V) loads per thread per tile
+constexpr int kCols = kNW * kCB * 32;  // (row, head) columns per work-group
+constexpr int kTileBytes = kBN * 256;  // one K (or V) tile: 64 rows of 256 bytes, swizzled
+constexpr int kMaxLevels = 4096;       // query tiles per sequence the schedule can order
 
 struct PrefillParams {
   const uint16_t* q;
@@ -95,7 +105,7 @@ __device__ __forceinline__ SeqInfo seq_info(const PrefillParams& p, int b) {
 constexpr int kPidWin = 2048;  // page ids staged in LDS per window (paged K/V)
 
 // Issue the loads of K/V tile `kt` (64 keys): thread tid brings the 16-byte
-// chunk `tid % 16` of rows tid/16 and tid/16 + 32, so 16 lanes read one whole
+// chunk `tid % 16` of rows tid/16 + (kNW * 4) * u, so 16 lanes read one whole
 // 256-byte row.  Loads are unconditional - straight-line code keeps the wait
 // counters exact - and rows that do not exist read a valid stand-in (key 0 of
 // the sequence, or page 0); `ok` marks the real rows for store_tile.
@@ -104,10 +114,9 @@ __device__ __forceinline__ void load_tile(const PrefillParams& p, const SeqInfo&
                                           int kt, int tid, const int* pids, int wbase,
                                           u32x4_t* kr, u32x4_t* vr, bool* ok) {
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int c = tid + u * (kNW * 64);
-    const int row = c >> 4;
-    const int piece = c & 15;
+  for (int u = 0; u < kLoadIters; ++u) {
+    const int row = (tid >> 4) + kNW * 4 * u;
+    const int piece = tid & 15;
     const int key = kt * kBN + row;
     int64_t off;
     if (!PAGED) {
@@ -127,27 +136,60 @@ __device__ __forceinline__ void load_tile(const PrefillParams& p, const SeqInfo&
   }
 }
 
-__device__ __forceinline__ void store_tile(uint16_t* ks, uint16_t* vs, int tid, const u32x4_t* kr,
-                                           const u32x4_t* vr, const bool* ok) {
+__device__ __forceinline__ void store_tile(unsigned char* ks, unsigned char* vs, int tid,
+                                           const u32x4_t* kr, const u32x4_t* vr, const bool* ok) {
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int c = tid + u * (kNW * 64);
-    const int row = c >> 4;
-    const int piece = c & 15;
+  for (int u = 0; u < kLoadIters; ++u) {
+    const int off = swz_off((tid >> 4) + kNW * 4 * u, tid & 15);
     const u32x4_t z = u32x4_t{0, 0, 0, 0};
-    *reinterpret_cast<u32x4_t*>(ks + row * kRow + piece * 8) = ok[u] ? kr[u] : z;
-    *reinterpret_cast<u32x4_t*>(vs + row * kRow + piece * 8) = ok[u] ? vr[u] : z;
+    *reinterpret_cast<u32x4_t*>(ks + off) = ok[u] ? kr[u] : z;
+    *reinterpret_cast<u32x4_t*>(vs + off) = ok[u] ? vr[u] : z;
   }
 }
 
+// Query tiles of one sequence, or 0 if its metadata is invalid.
+template <bool PAGED>
+__device__ __forceinline__ int seq_tiles(const PrefillParams& p, int b) {
+  const SeqInfo si = seq_info<PAGED>(p, b);
+  return si.code == 0 ? (si.qlen + p.bm - 1) / p.bm : 0;
+}
+
+// In-place suffix sum over a[0 .. n) in LDS: a[t] <- a[t] + a[t+1] + ... .
+__device__ __forceinline__ void lds_suffix_sum(int* a, int n, int* tot, int tid) {
+  constexpr int kThreads = kNW * 64;
+  const int per = (n + kThreads - 1) / kThreads;
+  const int lo = min(tid * per, n), hi = min(lo + per, n);
+  int sum = 0;
+  for (int u = lo; u < hi; ++u) sum += a[u];
+  tot[tid] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int u = tid + 1; u < kThreads; ++u) run += tot[u];
+  __syncthreads();
+  for (int u = hi - 1; u >= lo; --u) {
+    run += a[u];
+    a[u] = run;
+  }
+  __syncthreads();
+}
+
+// Persistent kernel: gridDim.x work-groups (one per CU) share a schedule of
+// every (sequence, query tile, kv head, head tile) item, ordered by query-tile
+// index from the last down (the longest causal tiles first) and striped over
+// the work-groups.  Each group derives the same schedule from the metadata:
+// a histogram of per-sequence tile counts gives, for every tile index t, how
+// many sequences have a tile t and how many items precede that level.  No
+// work-group is ever idle, which matters because the hardware dispatches
+// groups in order and round-robin over CUs: a regular pattern of instantly
+// finishing groups would pin the live ones to a fraction of the CUs.
 template <bool PAGED, int LAYOUT>
 __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
-  __shared__ __align__(16) uint16_t smem[4 * kTileElems];  // K0, V0, K1, V1
+  __shared__ __align__(16) unsigned char smem[4 * kTileBytes];  // K0, V0, K1, V1
   __shared__ int pids[PAGED ? kPidWin : 1];
-  const int kvh = blockIdx.x / p.head_tiles;
-  const int ht = blockIdx.x - kvh * p.head_tiles;
-  const int b = blockIdx.y;
-  const int tile = p.num_tiles - 1 - (int)blockIdx.z;
+  __shared__ int lvl_cnt[kMaxLevels + 1];   // sequences with more than t tiles
+  __shared__ int lvl_before[kMaxLevels + 1];  // items at tile indices above t
+  __shared__ int red[kNW * 64];
+  __shared__ int sel_b;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -155,54 +197,132 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
   const int gi = lane >> 5;
   const int g16 = (lane >> 4) & 1;
   const int i16 = lane & 15;
+  const int G = gridDim.x;
+
+  // ---- per-sequence status: this group covers sequences b = blockIdx.x mod G
+  if (p.status != nullptr) {
+    for (int b = blockIdx.x; b < p.batch; b += G) {
+      const SeqInfo si = seq_info<PAGED>(p, b);
+      int code = si.code;
+      if (PAGED && code == 0) {
+        const int need = (si.klen + kPage - 1) / kPage;
+        int bad = 0;
+        for (int i = tid; i < need; i += kNW * 64) {
+          const int pid = p.page_indices[si.kbase + i];
+          bad |= (pid < 0 || pid >= p.num_pages);
+        }
+        if (__syncthreads_or(bad)) code = kStatusPageRange;
+      }
+      if (tid == 0) p.status[b] = code;
+    }
+  }
+
+  // ---- the schedule ------------------------------------------------------
+  const int levels = p.num_tiles;  // <= kMaxLevels (host-checked)
+  for (int t = tid; t <= levels; t += kNW * 64) lvl_cnt[t] = 0;
+  __syncthreads();
+  for (int b = tid; b < p.batch; b += kNW * 64) {
+    const int n = min(seq_tiles<PAGED>(p, b), levels);
+    if (n > 0) atomicAdd(&lvl_cnt[n], 1);  // histogram of tile counts
+  }
+  __syncthreads();
+  lds_suffix_sum(lvl_cnt, levels + 1, red, tid);  // lvl_cnt[n] = #sequences with >= n tiles
+  for (int t = tid; t <= levels; t += kNW * 64)
+    lvl_before[t] = t + 1 <= levels ? lvl_cnt[t + 1] : 0;  // #sequences with tile t
+  __syncthreads();
+  // lvl_before[t] <- items (pairs) at levels >= t, then shift to levels > t
+  lds_suffix_sum(lvl_before, levels + 1, red, tid);
+  const int total_pairs = lvl_before[0];
+  const int per_pair = p.hkv * p.head_tiles;
+  const int64_t total_items = (int64_t)total_pairs * per_pair;
+
+  // Deal items to groups boustrophedon-style in units of 8 consecutive items
+  // (same tile index, neighbouring kv heads): even rounds go 0 .. G-1, odd
+  // rounds G-1 .. 0, so each group pairs long tiles with short ones, while an
+  // item's position mod 8 - its XCD - is kept.
+  const int G8 = G >= 8 ? G / 8 : 1;
+  const int gsub = G >= 8 ? (int)(blockIdx.x & 7) : 0;
+  const int gblk = G >= 8 ? (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+  const int gw = G >= 8 ? 8 : G;
+  for (int64_t round = 0; round * G < total_items; ++round) {
+    const int64_t slot = (round & 1) ? (int64_t)(G8 - 1 - gblk) * gw + gsub : (int64_t)blockIdx.x;
+    const int64_t item = round * G + slot;
+    if (item >= total_items) continue;
+    const int j = (int)(item / per_pair);
+    const int kvh = (int)((item / p.head_tiles) % p.hkv);
+    const int ht = (int)(item % p.head_tiles);
+    // level t: the smallest t whose later levels hold at most j pairs
+    int lo_t = 0, hi_t = levels - 1;
+    while (lo_t < hi_t) {
+      const int mid = (lo_t + hi_t) >> 1;
+      if (lvl_before[mid + 1] <= j) hi_t = mid; else lo_t = mid + 1;
+    }
+    const int tile = lo_t;
+    const int rank = j - lvl_before[tile + 1];
+    // sequence: the rank-th (ascending) with more than `tile` tiles
+    {
+      int seen = 0;
+      for (int b0 = 0; b0 < p.batch; b0 += kNW * 64) {
+        const int bb = b0 + tid;
+        const bool has = bb < p.batch && seq_tiles<PAGED>(p, bb) > tile;
+        const uint64_t mask = __builtin_amdgcn_ballot_w64(has);
+        const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+        if (lane == 0) red[wave] = __builtin_popcountll(mask);
+        __syncthreads();
+        int before = 0, chunk = 0;
+        for (int w = 0; w < kNW; ++w) {
+          before += w < wave ? red[w] : 0;
+          chunk += red[w];
+        }
+        if (has && seen + before + pos == rank) sel_b = bb;
+        __syncthreads();
+        seen += chunk;
+        if (seen > rank) break;
+      }
+      __syncthreads();
+    }
+    const int b = sel_b;
 
   SeqInfo si = seq_info<PAGED>(p, b);
-
-  if (p.status != nullptr && blockIdx.x == 0 && tile == 0) {
-    int code = si.code;
-    if (PAGED && code == 0) {
-      const int need = (si.klen + kPage - 1) / kPage;
-      int bad = 0;
-      for (int i = tid; i < need; i += kNW * 64) {
-        const int pid = p.page_indices[si.kbase + i];
-        bad |= (pid < 0 || pid >= p.num_pages);
-      }
-      if (__syncthreads_or(bad)) code = kStatusPageRange;
-    }
-    if (tid == 0) p.status[b] = code;
-  }
-  if (si.code != 0) return;
   const int r0 = tile * p.bm;
-  if (r0 >= si.qlen) return;
   const int rows_here = min(p.bm, si.qlen - r0);
   const int offset = si.klen - si.qlen;  // bottom-right causal alignment
   const int kv_end = p.causal ? min(si.klen, r0 + rows_here + offset) : si.klen;
   const int ntiles = (kv_end + kBN - 1) / kBN;
 
-  // this lane's column: (row, head) pair
-  const int pair = wave * 32 + col;
-  const int prow = pair / p.gwg;
-  const int phead_t = pair - prow * p.gwg;
-  const int head_in_group = ht * p.gwg + phead_t;
-  const bool col_ok = prow < rows_here && pair < p.bm * p.gwg && head_in_group < p.group;
-  const int qrow = r0 + prow;                  // row index within the sequence
-  const int head = kvh * p.group + head_in_group;
-  const int row_lim = qrow + offset;           // last visible key (causal)
-
-  u32x4_t qf[8];
-  if (col_ok) {
-    const uint16_t* qp = p.q + ((int64_t)(si.q0 + qrow) * p.hq + head) * kHeadDim + gi * 64;
+  // this lane's columns: (row, head) pairs wave*32*kCB + cb*32 + col
+  bool col_ok[kCB];
+  int qrow[kCB], head[kCB], row_lim[kCB];
+  u32x4_t qf[kCB][8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = ldg16(qp + 8 * s);
-  } else {
+  for (int cb = 0; cb < kCB; ++cb) {
+    const int pair = wave * (kCB * 32) + cb * 32 + col;
+    const int prow = pair / p.gwg;
+    const int head_in_group = ht * p.gwg + (pair - prow * p.gwg);
+    col_ok[cb] = prow < rows_here && pair < p.bm * p.gwg && head_in_group < p.group;
+    qrow[cb] = r0 + prow;
+    head[cb] = kvh * p.group + head_in_group;
+    row_lim[cb] = qrow[cb] + offset;  // last visible key (causal)
+    if (col_ok[cb]) {
+      const uint16_t* qp =
+          p.q + ((int64_t)(si.q0 + qrow[cb]) * p.hq + head[cb]) * kHeadDim + gi * 64;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = u32x4_t{0, 0, 0, 0};
+      for (int st = 0; st < 8; ++st) qf[cb][st] = ldg16(qp + 8 * st);
+    } else {
+#pragma unroll
+      for (int st = 0; st < 8; ++st) qf[cb][st] = u32x4_t{0, 0, 0, 0};
+    }
   }
 
-  f32x16_t acc[4];
+  f32x16_t acc[kCB][4];
 #pragma unroll
-  for (int d = 0; d < 4; ++d) acc[d] = f32x16_t{};
-  float m = -INFINITY, lsum = 0.f;
+  for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) acc[cb][d] = f32x16_t{};
+  float m[kCB], lsum[kCB];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) { m[cb] = -INFINITY; lsum[cb] = 0.f; }
   // smallest visible-key limit among the work-group's rows: tiles past it need masks
   const int wg_min_lim = r0 + offset;
 
@@ -225,20 +345,20 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
   if (PAGED) stage_pids(0);
   __syncthreads();
 
-  u32x4_t kr[2], vr[2];
-  bool okr[2];
+  u32x4_t kr[kLoadIters], vr[kLoadIters];
+  bool okr[kLoadIters];
   if (ntiles > 0) {
     load_tile<PAGED, LAYOUT>(p, si, kvh, 0, tid, pids, wbase, kr, vr, okr);
-    store_tile(smem, smem + kTileElems, tid, kr, vr, okr);
+    store_tile(smem, smem + kTileBytes, tid, kr, vr, okr);
   }
   __syncthreads();
 
   for (int kt = 0; kt < ntiles; ++kt) {
-    const uint16_t* ks = smem + (kt & 1) * 2 * kTileElems;
-    const uint16_t* vs = ks + kTileElems;
+    const unsigned char* ks = smem + (kt & 1) * 2 * kTileBytes;
+    const unsigned char* vs = ks + kTileBytes;
     if (PAGED && kt + 1 < ntiles && (kt + 1) % kTilesPerWin == 0) {
-      // the next tile starts a new page-id window (every waves' reads of the
-      // current window are done: only tile kt+1 uses page ids from here on)
+      // the next tile starts a new page-id window (only tile kt+1 uses page
+      // ids from here on, and every wave is past its reads of the old window)
       wbase = (kt + 1) / kTilesPerWin * kPidWin;
       __syncthreads();
       stage_pids(wbase);
@@ -246,103 +366,115 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
     }
     if (kt + 1 < ntiles) load_tile<PAGED, LAYOUT>(p, si, kvh, kt + 1, tid, pids, wbase, kr, vr, okr);
 
-    // S^T[key][col] for the 64 keys of the tile: 2 key blocks x 8 k-steps
-    f32x16_t s[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      s[mb] = f32x16_t{};
-      const uint16_t* krow = ks + (mb * 32 + col) * kRow + gi * 64;
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(krow + 8 * st);
-        s[mb] = mfma_32x32x16(a, qf[st], s[mb]);
-      }
-    }
-
     const int key0 = kt * kBN;
     const bool need_mask = (key0 + kBN > si.klen) || (p.causal && key0 + kBN - 1 > wg_min_lim);
-    float mt = -INFINITY;
-    if (need_mask) {
+    // Two online-softmax steps of 32 keys per tile (keeps half the scores live).
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb) {
+      // S^T[key][col] for keys 32*mb .. +31: 8 k-steps; each K operand read
+      // from LDS serves both column blocks
+      f32x16_t s[kCB];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + mb * 32 + 8 * (r >> 2) + 4 * gi + (r & 3);
-          const bool vis = key < si.klen && (!p.causal || key <= row_lim);
-          s[mb][r] = vis ? s[mb][r] * p.scale_log2 : -INFINITY;
-          mt = fmaxf(mt, s[mb][r]);
-        }
-    } else {
+      for (int cb = 0; cb < kCB; ++cb) s[cb] = f32x16_t{};
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int st = 0; st < 8; ++st) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(ks + swz_off(mb * 32 + col, 8 * gi + st));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[mb][r] *= p.scale_log2;
-          mt = fmaxf(mt, s[mb][r]);
-        }
-    }
-    mt = pair_max32(mt);
-    const float mnew = fmaxf(m, mt);
-    const float muse = mnew == -INFINITY ? 0.f : mnew;
-    float psum = 0.f;
-    uint32_t pk[16];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = exp2f(s[mb][r] - muse);
-        const float p1 = exp2f(s[mb][r + 1] - muse);
-        psum += p0 + p1;
-        pk[mb * 8 + (r >> 1)] = pack_bf16x2(p0, p1);
+        for (int cb = 0; cb < kCB; ++cb) s[cb] = mfma_32x32x16(a, qf[cb][st], s[cb]);
       }
-    if (__builtin_amdgcn_ballot_w64(mnew != m) != 0) {  // rescale only when a max moved
-      const float corr = exp2f(m - muse);
-      lsum *= corr;
+      uint32_t pk[kCB][8];
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
+      for (int cb = 0; cb < kCB; ++cb) {
+        float mraw = -INFINITY;
+        if (need_mask) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[d][r] *= corr;
-    }
-    lsum += psum;
-    m = mnew;
-
-    // O^T += V^T * P^T over 4 k-steps of 16 keys
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + mb * 32 + 8 * (r >> 2) + 4 * gi + (r & 3);
+            const bool vis = key < si.klen && (!p.causal || key <= row_lim[cb]);
+            s[cb][r] = vis ? s[cb][r] : -INFINITY;
+            mraw = fmaxf(mraw, s[cb][r]);
+          }
+        } else {
 #pragma unroll
-    for (int ks4 = 0; ks4 < 4; ++ks4) {
-      const u32x4_t pf = u32x4_t{pk[4 * ks4], pk[4 * ks4 + 1], pk[4 * ks4 + 2], pk[4 * ks4 + 3]};
-      const uint16_t* vrow = vs + (16 * ks4 + 4 * gi + (i16 >> 2)) * kRow + 16 * g16 + 4 * (i16 & 3);
+          for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, s[cb][r]);
+        }
+        // raw-score max (the scale is >= 0, so it commutes with max), then
+        // lazy rescaling: the reference max moves only when exceeded by 2^8
+        const float mt = pair_max32(mraw) * p.scale_log2;
+        if (__builtin_amdgcn_ballot_w64(mt > m[cb] + 8.f) != 0) {
+          const float mnew = mt > m[cb] + 8.f ? mt : m[cb];
+          const float corr = fast_exp2(m[cb] - mnew);  // 0 while m is still -inf
+          lsum[cb] *= corr;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const u32x2_t a0 = lds_read_tr16(vrow + 32 * d);
-        const u32x2_t a1 = lds_read_tr16(vrow + 8 * kRow + 32 * d);
-        acc[d] = mfma_32x32x16(u32x4_t{a0[0], a0[1], a1[0], a1[1]}, pf, acc[d]);
+          for (int d = 0; d < 4; ++d)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[cb][d][r] *= corr;
+          m[cb] = mnew;
+        }
+        const float muse = m[cb] == -INFINITY ? 0.f : m[cb];
+        float psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(fmaf(s[cb][r], p.scale_log2, -muse));
+          const float p1 = fast_exp2(fmaf(s[cb][r + 1], p.scale_log2, -muse));
+          psum += p0 + p1;
+          pk[cb][r >> 1] = pack_bf16x2(p0, p1);
+        }
+        lsum[cb] += psum;
+      }
+      // O^T += V^T * P^T over the 2 k-steps of 16 keys in this block; each V^T
+      // operand serves both column blocks.  Transpose read: lanes 4e..4e+3 of
+      // a 16-lane group address row (32*mb + 16*h + 4*(l/32) + e) (then +8),
+      // 16 dims of the 32-wide d block.
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 32 * mb + 16 * h + 4 * gi + (i16 >> 2);
+        const int b8 = 8 * (i16 & 1);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int c = 4 * d + 2 * g16 + ((i16 & 3) >> 1);
+          const u32x2_t a0 = lds_read_tr16(reinterpret_cast<const uint16_t*>(vs + swz_off(r, c) + b8));
+          const u32x2_t a1 = lds_read_tr16(reinterpret_cast<const uint16_t*>(vs + swz_off(r + 8, c) + b8));
+          const u32x4_t a = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+#pragma unroll
+          for (int cb = 0; cb < kCB; ++cb) {
+            const u32x4_t pf = u32x4_t{pk[cb][4 * h], pk[cb][4 * h + 1], pk[cb][4 * h + 2],
+                                       pk[cb][4 * h + 3]};
+            acc[cb][d] = mfma_32x32x16(a, pf, acc[cb][d]);
+          }
+        }
       }
     }
 
     if (kt + 1 < ntiles) {
-      uint16_t* kn = smem + ((kt + 1) & 1) * 2 * kTileElems;
-      store_tile(kn, kn + kTileElems, tid, kr, vr, okr);
+      unsigned char* kn = smem + ((kt + 1) & 1) * 2 * kTileBytes;
+      store_tile(kn, kn + kTileBytes, tid, kr, vr, okr);
     }
     __syncthreads();
   }
 
-  lsum = pair_sum32(lsum);
-  if (!col_ok) return;
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  uint16_t* orow = p.o + ((int64_t)(si.q0 + qrow) * p.hq + head) * kHeadDim;
 #pragma unroll
-  for (int d = 0; d < 4; ++d)
+  for (int cb = 0; cb < kCB; ++cb) {
+    const float ls = pair_sum32(lsum[cb]);
+    if (!col_ok[cb]) continue;
+    const float inv = ls > 0.f ? 1.f / ls : 0.f;
+    uint16_t* orow = p.o + ((int64_t)(si.q0 + qrow[cb]) * p.hq + head[cb]) * kHeadDim;
 #pragma unroll
-    for (int r = 0; r < 16; r += 4) {
-      const int dd = 32 * d + 8 * (r >> 2) + 4 * gi;
-      u32x2_t w;
-      w[0] = pack_bf16x2(acc[d][r] * inv, acc[d][r + 1] * inv);
-      w[1] = pack_bf16x2(acc[d][r + 2] * inv, acc[d][r + 3] * inv);
-      *reinterpret_cast<u32x2_t*>(orow + dd) = w;
-    }
-  if (gi == 0 && p.lse != nullptr)
-    p.lse[(int64_t)(si.q0 + qrow) * p.hq + head] =
-        lsum > 0.f ? (m + __log2f(lsum)) * kLn2 : -INFINITY;
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        const int dd = 32 * d + 8 * (r >> 2) + 4 * gi;
+        u32x2_t w;
+        w[0] = pack_bf16x2(acc[cb][d][r] * inv, acc[cb][d][r + 1] * inv);
+        w[1] = pack_bf16x2(acc[cb][d][r + 2] * inv, acc[cb][d][r + 3] * inv);
+        *reinterpret_cast<u32x2_t*>(orow + dd) = w;
+      }
+    if (gi == 0 && p.lse != nullptr)
+      p.lse[(int64_t)(si.q0 + qrow[cb]) * p.hq + head[cb]] =
+          ls > 0.f ? (m[cb] + __log2f(ls)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();  // LDS (tiles, page ids, selection) is reused by the next item
+  }
 }
 
 }  // namespace
@@ -376,7 +508,17 @@ hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream) {
   p.num_pages = a.num_pages;
   p.num_page_entries = a.num_page_entries;
   p.scale_log2 = a.sm_scale * kLog2e;
-  dim3 grid(p.hkv * p.head_tiles, p.batch, p.num_tiles);
+  // one persistent work-group per CU (a multiple of 8, so a kv head's items
+  // stay on one XCD), never more than there can be items
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t pairs_ub = ((int64_t)a.nnz_qo + p.bm - 1) / p.bm + a.batch;
+  const int64_t items_ub = pairs_ub * p.hkv * p.head_tiles;
+  int64_t groups = cus >= 8 ? (cus / 8) * 8 : (cus > 0 ? cus : 1);
+  if (groups > items_ub) groups = items_ub > 0 ? items_ub : 1;
+  dim3 grid((unsigned)groups);
   dim3 block(kNW * 64);
   if (!a.paged)
     hipLaunchKernelGGL((prefill_kernel<false, 0>), grid, block, 0, stream, p);
