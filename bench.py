@@ -196,9 +196,13 @@ def bench_append_and_paged_prefill(torch, oxa, case, iters, warmup):
     stream = torch.cuda.current_stream()
     hkv = kv.num_kv_heads
 
+    ws_a = torch.empty(oxa.oxa_paged_append_rope_workspace_bytes(case.k.shape[0]),
+                       dtype=torch.uint8, device="cuda")
+
     def append(i):
         rc = oxa.oxa_paged_append_rope(q_in, q_rot, k_in, v_in, bi, pos, kp, vp, indptr, ids, rc_t,
-                                       status, layout=kv.layout, rope_theta=case.rope_theta)
+                                       status, layout=kv.layout, rope_theta=case.rope_theta,
+                                       workspace=ws_a)
         if rc != 0:
             raise RuntimeError(oxa.status_string(rc))
 

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define OXA_ABI_VERSION 1
+#define OXA_ABI_VERSION 2
 #define OXA_PAGE_SIZE 16
 #define OXA_HEAD_DIM 128
 
@@ -117,20 +117,25 @@ const char* oxa_status_string(int32_t code);
  * double precision), (x_i cos a - x_{i+64} sin a, x_{i+64} cos a + x_i sin a),
  * rounded once to bf16.
  *
- * All or nothing: a first kernel checks every token (batch index in
+ * All or nothing: a check pass validates every token (batch index in
  * [0, batch), position in [0, 16 * pages listed for b), page id in
- * [0, num_pages), page_refcounts[page] == 1) and writes status[0] = 0 or the
+ * [0, num_pages), page_refcounts[page] == 1) and records, per work-group, the
+ * smallest failing token in the workspace; the writing kernel reduces those
+ * records first and writes only if no token failed.  status[0] = 0 or the
  * OXA_DEV_* code of the lowest failing token, status[1] = that token or -1.
- * The writing kernel runs only if status[0] == 0; otherwise no pool byte and
- * no q_out byte changes.  Two tokens naming the same (page, slot) break the
- * contract (the result is unspecified).
+ * On failure no pool byte and no q_out byte changes.  Two tokens naming the
+ * same (page, slot) break the contract (the result is unspecified).
  *
  * Shapes: q_in/q_out [nnz][num_qo_heads][128]; k_in/v_in [nnz][num_kv_heads][128];
  * batch_indices/positions [nnz]; page_indptr [batch+1];
  * page_indices [num_page_entries]; page_refcounts [num_pages]; status [2].
  * q_out may equal q_in (in place) but may not overlap it otherwise; q_in and
  * q_out are both NULL or both non-NULL (num_qo_heads is then ignored).
- * Ranges: 0 <= nnz (0 = no-op apart from status), 1 <= batch.
+ * workspace: device scratch of oxa_paged_append_rope_workspace_bytes(nnz)
+ * bytes (16-byte aligned, any contents), used for the call only.
+ * Ranges: 0 <= nnz (0 = no-op apart from status; the per-token pointers
+ * q_in, q_out, k_in, v_in, batch_indices, positions may then be NULL),
+ * 1 <= batch.
  */
 oxa_status oxa_paged_append_rope(
     hipStream_t stream,
@@ -141,7 +146,11 @@ oxa_status oxa_paged_append_rope(
     const int32_t* page_indptr, int32_t batch,
     const int32_t* page_indices, int32_t num_page_entries,
     const int32_t* page_refcounts, float rope_theta,
+    void* workspace, size_t workspace_bytes,
     int32_t* status);
+
+/* Workspace bytes oxa_paged_append_rope needs (8192, whatever nnz is). */
+size_t oxa_paged_append_rope_workspace_bytes(int32_t nnz);
 
 /*
  * Paged batch decode: one query token per sequence over its paged KV.

@@ -50,7 +50,8 @@ SIGNATURES = {
     "oxa_abi_version": (_I, []),
     "oxa_status_string": (ctypes.c_char_p, [_I]),
     "oxa_paged_append_rope": (_I, [_P, _P, _P, _I, _P, _P, _I, _I, _P, _P, _I, _P, _P, _I, _I, _I,
-                                   _P, _I, _P, _I, _P, _F, _P]),
+                                   _P, _I, _P, _I, _P, _F, _P, _Z, _P]),
+    "oxa_paged_append_rope_workspace_bytes": (_Z, [_I]),
     "oxa_paged_decode": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _P, _P, _I, _P, _I, _F,
                               _I, _P, _Z, _P, _P, _P]),
     "oxa_paged_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
@@ -145,25 +146,37 @@ def _layout(layout) -> int:
 
 # ------------------------------------------------------------------ entry points
 
+def oxa_paged_append_rope_workspace_bytes(nnz) -> int:
+    return int(lib().oxa_paged_append_rope_workspace_bytes(nnz))
+
+
 def oxa_paged_append_rope(q_in, q_out, k_in, v_in, batch_indices, positions, k_pages, v_pages,
                           page_indptr, page_indices, page_refcounts, status, *, layout="NHD",
-                          rope_theta=10000.0, stream=None) -> int:
+                          rope_theta=10000.0, workspace=None, stream=None) -> int:
     """Fused NeoX RoPE on q/k and append of (rotated k, v) into exclusive pages.
 
     q_in/q_out [nnz, Hq, 128] (both None to skip q), k_in/v_in [nnz, Hkv, 128],
-    pools in ``layout``, status int32 [2] (code, first failing token).
+    pools in ``layout``, status int32 [2] (code, first failing token).  Without
+    a ``workspace`` tensor one of oxa_paged_append_rope_workspace_bytes(nnz)
+    bytes is allocated on k_in's device.
     """
     lay = _layout(layout)
     hkv = k_in.shape[1]
     num_pages = k_pages.shape[0]
     hq = q_in.shape[1] if q_in is not None else 0
+    if workspace is None:
+        import torch
+        nbytes = oxa_paged_append_rope_workspace_bytes(k_in.shape[0])
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=k_in.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
     return lib().oxa_paged_append_rope(
         _stream(stream), _bf16(q_in, "q_in"), _bf16(q_out, "q_out"), hq, _bf16(k_in, "k_in"),
         _bf16(v_in, "v_in"), hkv, k_in.shape[2], _i32(batch_indices, "batch_indices"),
         _i32(positions, "positions"), k_in.shape[0], _bf16(k_pages, "k_pages"),
         _bf16(v_pages, "v_pages"), num_pages, PAGE_SIZE, lay, _i32(page_indptr, "page_indptr"),
         page_indptr.shape[0] - 1, _i32(page_indices, "page_indices"), page_indices.shape[0],
-        _i32(page_refcounts, "page_refcounts"), float(rope_theta), _i32(status, "status"))
+        _i32(page_refcounts, "page_refcounts"), float(rope_theta), _ptr(workspace), ws_bytes,
+        _i32(status, "status"))
 
 
 def oxa_paged_decode_workspace_bytes(batch, num_qo_heads, num_partitions, head_dim=HEAD_DIM) -> int:

@@ -9,8 +9,10 @@
 // with explicit positions; RoPE plus paged append).
 //
 // Two kernels keep the call all-or-nothing without a host round trip:
-//  1. one work-group checks every token and writes status[0..1];
-//  2. the writer kernel returns at once unless status[0] == 0.
+//  1. the check pass: each work-group validates a share of the tokens and
+//     records its smallest failing token in the workspace;
+//  2. the writer: every work-group first reduces those records and returns
+//     at once if any token failed; work-group 0 writes status[0..1].
 // Angles are evaluated in double precision (position * inv_freq, then sincos),
 // the rotation too, and each result is rounded once to bf16.  Positions reach
 // tens of thousands of radians, where a float angle would already be wrong in
@@ -39,6 +41,8 @@ struct AppendParams {
   const int32_t* page_indices;
   const int32_t* page_refcounts;
   int32_t* status;
+  int32_t* check;  // [check_groups][2]: smallest failing token, its code
+  int32_t check_groups;
   int32_t hq, hkv, nnz, num_pages, layout, batch, num_page_entries;
   double inv_freq[64];
 };
@@ -62,33 +66,82 @@ __device__ __forceinline__ int check_token(const AppendParams& p, int t, int* pa
   return 0;
 }
 
-// One work-group of 1024 threads.  Each thread checks a strided set of
-// tokens; the smallest failing token index wins.
-__global__ __launch_bounds__(1024) void append_check_kernel(AppendParams p) {
-  __shared__ int first_bad;
-  if (threadIdx.x == 0) first_bad = 0x7fffffff;
+constexpr int kNone = 0x7fffffff;        // "no failing token"
+constexpr int kCheckPer = 4;             // tokens per thread per pass
+constexpr int kCheckTile = 256 * kCheckPer;
+
+// Check pass: work-group g checks tokens g*1024 .. g*1024 + 1023 (then every
+// gridDim.x*1024 further) and records its smallest failing token and that
+// token's code in check[g] (kNone if all pass).  Per pass a thread issues the
+// loads of its 4 tokens together, one dependent level at a time (batch index
+// and position, then the indptr pair, then the page id, then its refcount),
+// through addresses that fall back to a valid dummy word once a token has
+// failed, so no load waits behind a branch.
+__global__ __launch_bounds__(256) void append_check_kernel(AppendParams p) {
+  __shared__ int first_bad, first_code;
+  const int tid = threadIdx.x;
+  if (tid == 0) first_bad = kNone;
   __syncthreads();
-  int my_t = 0x7fffffff, my_code = 0;
-  constexpr int kUnroll = 8;
-  for (int base = threadIdx.x; base < p.nnz && my_t == 0x7fffffff; base += 1024 * kUnroll) {
-    int codes[kUnroll];
+  const int* dummy = p.page_indptr;  // batch >= 1, so at least two words
+  int my_t = kNone, my_code = 0;
+  for (int base = blockIdx.x * kCheckTile; base < p.nnz && my_t == kNone;
+       base += gridDim.x * kCheckTile) {
+    // level 1: batch index and position
+    int x[kCheckPer], y[kCheckPer], code[kCheckPer];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int t = base + u * 1024;
-      int page;
-      codes[u] = t < p.nnz ? check_token(p, t, &page) : 0;
+    for (int u = 0; u < kCheckPer; ++u) {
+      const int t = base + u * 256 + tid;
+      const bool in = t < p.nnz;
+      x[u] = *(in ? p.batch_indices + t : dummy);
+      y[u] = *(in ? p.positions + t : dummy);
+    }
+    // level 2: the sequence's page range; x <- page-index slot or -1
+    int lo[kCheckPer], hi[kCheckPer];
+#pragma unroll
+    for (int u = 0; u < kCheckPer; ++u) {
+      const bool bok = x[u] >= 0 && x[u] < p.batch;
+      lo[u] = *(bok ? p.page_indptr + x[u] : dummy);
+      hi[u] = *(bok ? p.page_indptr + x[u] + 1 : dummy);
+      code[u] = bok ? 0 : kStatusBatchIndex;
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      if (codes[u] != 0 && my_t == 0x7fffffff) { my_t = base + u * 1024; my_code = codes[u]; }
+    for (int u = 0; u < kCheckPer; ++u) {
+      // an indptr that leaves the page-index array gives the sequence no capacity
+      const bool ptr_ok = lo[u] >= 0 && hi[u] >= lo[u] && hi[u] <= p.num_page_entries;
+      const int64_t cap = ptr_ok ? (int64_t)(hi[u] - lo[u]) * kPage : 0;
+      const bool pos_ok = y[u] >= 0 && (int64_t)y[u] < cap;
+      if (code[u] == 0 && !pos_ok) code[u] = kStatusCapacity;
+      x[u] = code[u] == 0 ? lo[u] + y[u] / kPage : -1;
+    }
+    // level 3: the page id; x <- page or -1
+#pragma unroll
+    for (int u = 0; u < kCheckPer; ++u) y[u] = *(x[u] >= 0 ? p.page_indices + x[u] : dummy);
+#pragma unroll
+    for (int u = 0; u < kCheckPer; ++u) {
+      const bool pg_ok = y[u] >= 0 && y[u] < p.num_pages;
+      if (code[u] == 0 && !pg_ok) code[u] = kStatusPageRange;
+      x[u] = code[u] == 0 ? y[u] : -1;
+    }
+    // level 4: the page's reference count
+#pragma unroll
+    for (int u = 0; u < kCheckPer; ++u) y[u] = *(x[u] >= 0 ? p.page_refcounts + x[u] : dummy);
+#pragma unroll
+    for (int u = 0; u < kCheckPer; ++u) {
+      const int t = base + u * 256 + tid;
+      if (code[u] == 0 && x[u] >= 0 && y[u] != 1) code[u] = kStatusNotExclusive;
+      if (t < p.nnz && code[u] != 0 && my_t == kNone) {
+        my_t = t;
+        my_code = code[u];
+      }
+    }
   }
-  if (my_t != 0x7fffffff) atomicMin(&first_bad, my_t);
+  if (my_t != kNone) atomicMin(&first_bad, my_t);
   __syncthreads();
-  if (first_bad == 0x7fffffff) {
-    if (threadIdx.x == 0) { p.status[0] = 0; p.status[1] = -1; }
-  } else if (my_t == first_bad) {
-    p.status[0] = my_code;
-    p.status[1] = my_t;
+  if (my_t != kNone && my_t == first_bad) first_code = my_code;  // one thread
+  __syncthreads();
+  if (tid == 0) {
+    p.check[2 * blockIdx.x] = first_bad;
+    p.check[2 * blockIdx.x + 1] = first_bad == kNone ? 0 : first_code;
   }
 }
 
@@ -140,7 +193,24 @@ __device__ __forceinline__ void rotate_chunk(u32x4_t w1, u32x4_t w2, const doubl
 template <int LAYOUT>
 __global__ __launch_bounds__(256) void append_rope_kernel(AppendParams p) {
   __shared__ double cs[4][64][2];
-  if (p.status[0] != 0) return;  // all-or-nothing gate
+  __shared__ int g_bad, g_code;
+  // All-or-nothing gate: every work-group reduces the check pass's records;
+  // work-group 0 reports the outcome.
+  if (threadIdx.x == 0) g_bad = kNone;
+  __syncthreads();
+  for (int i = threadIdx.x; i < p.check_groups; i += 256) {
+    const int tb = p.check[2 * i];
+    if (tb != kNone) atomicMin(&g_bad, tb);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < p.check_groups; i += 256)
+    if (g_bad != kNone && p.check[2 * i] == g_bad) g_code = p.check[2 * i + 1];
+  __syncthreads();
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    p.status[0] = g_bad == kNone ? 0 : g_code;
+    p.status[1] = g_bad == kNone ? -1 : g_bad;
+  }
+  if (g_bad != kNone) return;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int f = lane & 7;
@@ -201,6 +271,12 @@ __global__ __launch_bounds__(256) void append_rope_kernel(AppendParams p) {
 
 }  // namespace
 
+int append_check_groups(int nnz) {
+  int g = (nnz + kCheckTile - 1) / kCheckTile;
+  if (g > kAppendCheckGroups) g = kAppendCheckGroups;
+  return g < 1 ? 1 : g;
+}
+
 hipError_t launch_paged_append_rope(const AppendLaunch& a, hipStream_t stream) {
   AppendParams p;
   p.q_in = a.q_in;
@@ -223,11 +299,15 @@ hipError_t launch_paged_append_rope(const AppendLaunch& a, hipStream_t stream) {
   p.batch = a.batch;
   p.num_page_entries = a.num_page_entries;
   for (int i = 0; i < 64; ++i) p.inv_freq[i] = a.inv_freq[i];
-  hipLaunchKernelGGL(append_check_kernel, dim3(1), dim3(1024), 0, stream, p);
+  p.check = a.check;
+  p.check_groups = append_check_groups(a.nnz);
+  hipLaunchKernelGGL(append_check_kernel, dim3(p.check_groups), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.nnz == 0) return e;
+  if (e != hipSuccess) return e;
+  // the writer also reports the status, so it runs even for nnz == 0
   int blocks = (a.nnz + 3) / 4;
   if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
   if (a.layout == 0)
     hipLaunchKernelGGL(append_rope_kernel<0>, dim3(blocks), dim3(256), 0, stream, p);
   else

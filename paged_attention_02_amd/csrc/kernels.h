@@ -37,9 +37,13 @@ struct AppendLaunch {
   const int32_t* page_indices;
   const int32_t* page_refcounts;
   int32_t* status;
+  int32_t* check;  // workspace: [kAppendCheckGroups][2] per-work-group check records
   int32_t hq, hkv, nnz, num_pages, layout, batch, num_page_entries;
   double inv_freq[64];  // rope_theta^(-2i/128), i < 64, computed on the host in double
 };
+// Work-groups of the append check pass, at most: the workspace holds one
+// 8-byte record per work-group.
+constexpr int kAppendCheckGroups = 1024;
 hipError_t launch_paged_append_rope(const AppendLaunch& a, hipStream_t stream);
 
 struct PrefillLaunch {

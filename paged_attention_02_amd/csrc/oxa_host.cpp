@@ -92,6 +92,11 @@ const char* oxa_status_string(int32_t code) {
 
 // ---------------------------------------------------------------- append
 
+size_t oxa_paged_append_rope_workspace_bytes(int32_t nnz) {
+  (void)nnz;  // one record per check work-group, whatever the token count
+  return (size_t)oxa::kAppendCheckGroups * 8;
+}
+
 oxa_status oxa_paged_append_rope(hipStream_t stream, const uint16_t* q_in, uint16_t* q_out,
                                  int32_t num_qo_heads, const uint16_t* k_in,
                                  const uint16_t* v_in, int32_t num_kv_heads, int32_t head_dim,
@@ -101,9 +106,10 @@ oxa_status oxa_paged_append_rope(hipStream_t stream, const uint16_t* q_in, uint1
                                  const int32_t* page_indptr, int32_t batch,
                                  const int32_t* page_indices, int32_t num_page_entries,
                                  const int32_t* page_refcounts, float rope_theta,
-                                 int32_t* status) {
-  if (!k_in || !v_in || !batch_indices || !positions || !k_pages || !v_pages || !page_indptr ||
-      !page_indices || !page_refcounts || !status)
+                                 void* workspace, size_t workspace_bytes, int32_t* status) {
+  // with no tokens the per-token arrays may be absent (empty tensors)
+  if ((nnz != 0 && (!k_in || !v_in || !batch_indices || !positions)) || !k_pages || !v_pages ||
+      !page_indptr || !page_indices || !page_refcounts || !status)
     return OXA_ERR_NULL;
   if ((q_in == nullptr) != (q_out == nullptr)) return OXA_ERR_NULL;
   const bool has_q = q_in != nullptr;
@@ -115,8 +121,10 @@ oxa_status oxa_paged_append_rope(hipStream_t stream, const uint16_t* q_in, uint1
   if (!aligned(q_in, 16) || !aligned(q_out, 16) || !aligned(k_in, 16) || !aligned(v_in, 16) ||
       !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(batch_indices, 4) ||
       !aligned(positions, 4) || !aligned(page_indptr, 4) || !aligned(page_indices, 4) ||
-      !aligned(page_refcounts, 4) || !aligned(status, 4))
+      !aligned(page_refcounts, 4) || !aligned(status, 4) || !aligned(workspace, 16))
     return OXA_ERR_ALIGN;
+  const size_t need = oxa_paged_append_rope_workspace_bytes(nnz);
+  if (workspace == nullptr || workspace_bytes < need) return OXA_ERR_WORKSPACE;
 
   const uint64_t n = (uint64_t)nnz;
   const uint64_t qbytes = has_q ? n * (uint64_t)num_qo_heads * kRowBytes : 0;
@@ -132,13 +140,13 @@ oxa_status oxa_paged_append_rope(hipStream_t stream, const uint16_t* q_in, uint1
   // q_out == q_in (exactly) is the in-place form; any other overlap is rejected
   const bool in_place = has_q && q_out == q_in;
   const Region outs[] = {{k_pages, pool}, {v_pages, pool}, {status, 8},
-                         {in_place ? nullptr : q_out, qbytes}};
-  if (any_alias(outs, 4, ins, 8)) return OXA_ERR_ALIAS;
+                         {workspace, need}, {in_place ? nullptr : q_out, qbytes}};
+  if (any_alias(outs, 5, ins, 8)) return OXA_ERR_ALIAS;
   if (in_place) {
     const Region qr{q_in, qbytes};
     for (int i = 1; i < 8; ++i)
       if (overlaps(qr, ins[i])) return OXA_ERR_ALIAS;
-    for (int i = 0; i < 3; ++i)
+    for (int i = 0; i < 4; ++i)
       if (overlaps(qr, outs[i])) return OXA_ERR_ALIAS;
   }
 
@@ -155,6 +163,7 @@ oxa_status oxa_paged_append_rope(hipStream_t stream, const uint16_t* q_in, uint1
   a.page_indices = page_indices;
   a.page_refcounts = page_refcounts;
   a.status = status;
+  a.check = static_cast<int32_t*>(workspace);
   a.hq = has_q ? num_qo_heads : 0;
   a.hkv = num_kv_heads;
   a.nnz = nnz;

@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     lib = ensure_built()
-    assert lib.oxa_abi_version() == 1
+    assert lib.oxa_abi_version() == 2
     assert oxa.status_string(0) == "OXA_OK"
     assert oxa.status_string(20) == "OXA_DEV_NOT_EXCLUSIVE"
     assert oxa.status_string(999) == "unknown"
@@ -40,3 +40,6 @@ def test_workspace_queries():
     # the long MQA workload: 8 x 32 rows x 16 partitions x (128 + 1) floats
     assert oxa.oxa_paged_decode_workspace_bytes(8, 32, 16) == 8 * 32 * 16 * 129 * 4 == 2113536
     assert oxa.lib().oxa_ragged_prefill_workspace_bytes(4, 7680, 32, 128) == 0
+    # append: one 8-byte record per check work-group (at most 1024 of them)
+    assert oxa.oxa_paged_append_rope_workspace_bytes(32768) == 8192
+    assert oxa.oxa_paged_append_rope_workspace_bytes(0) == 8192

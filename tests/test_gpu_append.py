@@ -124,6 +124,40 @@ def test_rejections_write_nothing():
         assert (got["q_out"] == 0x1234).all()      # q_out untouched too
 
 
+def test_rejection_spread_over_check_groups():
+    # 5000 tokens: the check pass runs five work-groups of 1024 tokens each;
+    # the lowest failing token must win whichever group saw it, and a failure
+    # seen only by the last group must still stop every write.
+    case = W.append_case(29, seq_lens=[3000, 2000], num_qo_heads=4, num_kv_heads=2)
+    kv = case.kv
+    pos = case.positions.copy()
+    pos[4500] = 10 ** 6                            # far beyond sequence 1's pages
+    bi = case.batch_indices.copy()
+    bi[2100] = 7                                   # a sequence that does not exist
+    rc = case.page_refcounts.copy()
+    rc[kv.page_indices[kv.page_indptr[1] + 124]] = 0   # the page of token 3000 + 1984
+    for over in (dict(positions=pos), dict(batch_indices=bi), dict(refcounts=rc),
+                 dict(positions=pos, batch_indices=bi, refcounts=rc)):
+        reason, _, _, _ = oracle_append(case, **over)
+        bad = R.append_status(over.get("batch_indices", case.batch_indices),
+                              over.get("positions", case.positions), kv.page_indptr,
+                              kv.page_indices, over.get("refcounts", case.page_refcounts),
+                              kv.num_pages, 2)
+        note(f"append spread rejection {sorted(over)}")
+        got = run_append(case, **over)
+        assert got["status"].tolist() == [REASON[reason], bad[0]]
+        assert np.array_equal(got["k"], kv.k_pool) and np.array_equal(got["v"], kv.v_pool)
+        assert (got["q_out"] == 0x1234).all()
+
+
+def test_empty_append_reports_success():
+    case = W.append_case(31, seq_lens=[0, 0], num_qo_heads=4, num_kv_heads=1, extra_pages=1)
+    note("append nnz=0")
+    got = run_append(case)
+    assert got["status"].tolist() == [0, -1]
+    assert np.array_equal(got["k"], case.kv.k_pool) and np.array_equal(got["v"], case.kv.v_pool)
+
+
 def test_rope_append_full_size():
     # 2 x 16384 tokens, 32 q / 8 kv heads, positions 0..16383, 2048 exclusive pages
     case = W.rope_append_prefill()

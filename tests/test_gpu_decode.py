@@ -149,8 +149,63 @@ def test_page_reuse_and_determinism():
     note("decode page reuse")
     g1 = run_decode(case)
     g2 = run_decode(case, num_partitions=1)
+    o, lse = oracle_decode(case)
+    assert_attention_close(g1["o"], o, "shared pages")
+    # identical query rows over the same pages give identical bits
     assert np.array_equal(g1["o"][0], g1["o"][1])
+    # the same call twice gives the same bits
     assert np.array_equal(g1["o"], g2["o"]) and np.array_equal(g1["lse"], g2["lse"])
+
+
+def test_physical_page_order_is_invisible():
+    # Permute the pool's pages and remap the table: the work decomposition
+    # depends on lengths only, so the outputs keep every bit.
+    case = W.decode_case(13, batch=6, num_qo_heads=16, num_kv_heads=4,
+                         seq_lens=[5, 100, 333, 1024, 17, 700])
+    note("decode page order")
+    g1 = run_decode(case)
+    kv = case.kv
+    perm = np.random.default_rng(3).permutation(kv.num_pages)
+    inv = np.argsort(perm)
+    kv.k_pool = np.ascontiguousarray(kv.k_pool[perm])
+    kv.v_pool = np.ascontiguousarray(kv.v_pool[perm])
+    kv.page_indices = inv[kv.page_indices].astype(np.int32)
+    g2 = run_decode(case)
+    assert np.array_equal(g1["o"], g2["o"]) and np.array_equal(g1["lse"], g2["lse"])
+
+
+@pytest.mark.parametrize("P", [1, 4])
+def test_one_long_sequence(P):
+    # 20,000 tokens on one kv head, four q heads: with P = 4 the partitions
+    # hold 313 pages each, the last one a ragged 312.
+    case = W.decode_case(17, batch=1, num_qo_heads=4, num_kv_heads=1, seq_lens=[20000],
+                         num_partitions=P, poison=True)
+    note(f"decode one long sequence P={P}")
+    got = run_decode(case, with_ws_view=True)
+    o, lse = oracle_decode(case)
+    assert (got["status"] == 0).all()
+    assert_attention_close(got["o"], o, f"long single P={P}")
+    assert_lse_close(got["lse"], lse)
+    # a second call with other lengths, through the same code path
+    case2 = W.decode_case(18, batch=3, num_qo_heads=4, num_kv_heads=1,
+                          seq_lens=[9000, 33, 4000], num_partitions=P, poison=True)
+    got2 = run_decode(case2)
+    o2, lse2 = oracle_decode(case2)
+    assert (got2["status"] == 0).all()
+    assert_attention_close(got2["o"], o2, f"second call P={P}")
+
+
+def test_batch_of_300_short_sequences():
+    # 300 short sequences of mixed lengths
+    lens = [int(x) for x in np.random.default_rng(21).integers(1, 300, size=300)]
+    case = W.decode_case(21, batch=300, num_qo_heads=8, num_kv_heads=2, seq_lens=lens,
+                         poison=True)
+    note("decode batch 300")
+    got = run_decode(case)
+    o, lse = oracle_decode(case)
+    assert (got["status"] == 0).all()
+    assert_attention_close(got["o"], o, "batch 300")
+    assert_lse_close(got["lse"], lse)
 
 
 def test_device_status_flags_bad_sequences_only():

@@ -113,7 +113,8 @@ def call_append(**over):
     args = dict(stream=None, q_in=addr(0), q_out=addr(1), hq=8, k_in=addr(2), v_in=addr(3), hkv=2,
                 head_dim=128, bidx=addr(4), pos=addr(5), nnz=20, kp=addr(6), vp=addr(7),
                 num_pages=10, page_size=16, layout=0, indptr=addr(8), batch=2, indices=addr(9),
-                num_entries=10, refc=addr(10), theta=10000.0, status=addr(11))
+                num_entries=10, refc=addr(10), theta=10000.0, ws=addr(12), ws_bytes=8192,
+                status=addr(11))
     args.update(over)
     return ensure_built().oxa_paged_append_rope(*args.values())
 
@@ -133,6 +134,10 @@ def call_append(**over):
     (dict(q_out=addr(0) + 256), oxa.OXA_ERR_ALIAS),     # partial overlap with q_in
     (dict(kp=addr(2)), oxa.OXA_ERR_ALIAS),              # K pool over k_in
     (dict(status=addr(6) + 64), oxa.OXA_ERR_ALIAS),     # status inside the K pool
+    (dict(ws=None), oxa.OXA_ERR_WORKSPACE),
+    (dict(ws_bytes=8191), oxa.OXA_ERR_WORKSPACE),
+    (dict(ws=addr(12) + 8), oxa.OXA_ERR_ALIGN),
+    (dict(ws=addr(7) + 4096), oxa.OXA_ERR_ALIAS),       # workspace inside the V pool
     (dict(vp=addr(6) + 1024), oxa.OXA_ERR_ALIAS),       # V pool overlaps K pool
 ])
 def test_append_rejections(over, code):
