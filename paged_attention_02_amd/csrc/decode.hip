@@ -18,8 +18,9 @@
 // waves merge through LDS at the end.
 //
 // Per block a wave loads K and V rows with whole-cache-line loads (16 lanes
-// per 256-byte row) into registers while the previous block is computed from
-// LDS, then stages them into its LDS slice (XOR-swizzled rows).  S^T = K Q^T
+// per 256-byte row), marked non-temporal since each row is read once per
+// call, into registers while the previous block is computed from LDS, then
+// stages them into its LDS slice (XOR-swizzled rows).  S^T = K Q^T
 // takes 8 v_mfma_f32_16x16x32_bf16 (tokens are M, the q heads N); each lane
 // then holds one head and 8 tokens, so the softmax max is an in-register
 // reduction plus two lane exchanges, and the probabilities already form the
@@ -199,13 +200,13 @@ void paged_decode_kernel(DecodeParams p) {
       const uint16_t* vb = vbase + pb * page_elems + lane_off;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        bl.k[s] = ldg16(ka + 4 * s * row_stride);
-        bl.v[s] = ldg16(va + 4 * s * row_stride);
+        bl.k[s] = ldg16_nt(ka + 4 * s * row_stride);
+        bl.v[s] = ldg16_nt(va + 4 * s * row_stride);
       }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        bl.k[4 + s] = ldg16(kb + 4 * s * row_stride);
-        bl.v[4 + s] = ldg16(vb + 4 * s * row_stride);
+        bl.k[4 + s] = ldg16_nt(kb + 4 * s * row_stride);
+        bl.v[4 + s] = ldg16_nt(vb + 4 * s * row_stride);
       }
     };
 

@@ -115,6 +115,12 @@ __device__ __forceinline__ u32x4_t ldg16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
 
+// 16 bytes with the non-temporal hint, for data that one call reads once
+// (streamed K/V rows): it keeps those lines from displacing reusable ones.
+__device__ __forceinline__ u32x4_t ldg16_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
 // 8 bytes through the LDS transpose read; `p` is a generic pointer into LDS.
 __device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
   i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));

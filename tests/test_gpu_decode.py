@@ -229,3 +229,60 @@ def test_device_status_flags_bad_sequences_only():
     # length above the declared maximum
     got = run_decode(case, max_seq_len=39)
     assert got["status"][0] == oxa.OXA_DEV_SEQ_LEN
+
+
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+@pytest.mark.parametrize("P", [1, 3])
+def test_batch_64_mixed_lengths(layout, P):
+    # 64 sequences of 1 to 3000 tokens: every output is checked, and with
+    # P > 1 every partition state in the workspace.
+    lens = [int(x) for x in np.random.default_rng(31).integers(1, 3000, size=64)]
+    lens[5] = 1
+    lens[9] = 3000
+    case = W.decode_case(31 + P, batch=64, num_qo_heads=8, num_kv_heads=2, seq_lens=lens,
+                         num_partitions=P, layout=layout, poison=True)
+    note(f"decode batch 64 mixed {layout} P={P}")
+    got = run_decode(case, with_ws_view=True)
+    o, lse = oracle_decode(case)
+    assert (got["status"] == 0).all()
+    assert_attention_close(got["o"], o, f"batch 64 {layout} P={P}")
+    assert_lse_close(got["lse"], lse)
+    if P > 1:
+        kv = case.kv
+        op, lp = A.decode_partials(case.q, kv.k_pool, kv.v_pool, kv.layout, kv.page_indptr,
+                                   kv.page_indices, kv.seq_lens, case.sm_scale, P,
+                                   case.max_seq_len)
+        live = np.isfinite(lp)
+        assert np.array_equal(np.isfinite(got["lse_part"]), live)
+        np.testing.assert_allclose(got["lse_part"][live], lp[live], rtol=1e-4, atol=2e-4)
+        assert not got["o_part"][~live].any()
+        err = got["o_part"][live] - op[live]
+        assert np.max(np.abs(err)) <= 2e-2
+        assert np.linalg.norm(err) / np.linalg.norm(op[live]) <= 5e-3
+
+
+def test_bad_sequences_among_80():
+    # Invalid sequences among 80: each bad one is flagged, and the valid ones
+    # around them still come out right.
+    lens = [int(x) for x in np.random.default_rng(41).integers(500, 2500, size=80)]
+    case = W.decode_case(41, batch=80, num_qo_heads=8, num_kv_heads=2, seq_lens=lens,
+                         poison=True)
+    kv = case.kv
+    kv.seq_lens[3] = 0                                    # empty
+    kv.page_indices[kv.page_indptr[7] + 1] = kv.num_pages  # a page id outside the pool
+    kv.seq_lens[11] = int(kv.page_indptr[12] - kv.page_indptr[11]) * 16 + 1  # too few pages
+    msl = int(kv.seq_lens.max())
+    note("decode bad sequences among 80")
+    got = run_decode(case, max_seq_len=msl)
+    want = [0] * 80
+    want[3], want[7], want[11] = oxa.OXA_DEV_SEQ_LEN, oxa.OXA_DEV_PAGE_RANGE, oxa.OXA_DEV_INDPTR
+    assert got["status"].tolist() == want
+    good = [b for b in range(80) if want[b] == 0]
+    indptr, idx = [0], []
+    for b in good:
+        idx.extend(kv.page_indices[kv.page_indptr[b]:kv.page_indptr[b + 1]])
+        indptr.append(len(idx))
+    o, _ = A.paged_decode(case.q[good], kv.k_pool, kv.v_pool, kv.layout,
+                          np.array(indptr, np.int32), np.array(idx, np.int32),
+                          kv.seq_lens[good], case.sm_scale)
+    assert_attention_close(got["o"][good], o, "valid sequences among bad ones")
