@@ -35,7 +35,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, TFLOP/s
-ROWS = ("decode", "decode_mha", "decode_mqa", "prefill_ragged", "append", "prefill_paged", "copy")
+ROWS = ("decode", "decode_mha", "decode_mqa", "prefill_ragged", "append", "prefill_paged",
+        "pages_shapes", "copy")
 
 
 def log(msg):
@@ -236,6 +237,59 @@ def bench_append_and_paged_prefill(torch, oxa, case, iters, warmup):
                 prefill_flops=causal_flops(qlens, kv.seq_lens, hq))
 
 
+def bench_pages_shapes(torch, oxa, W, iters=200, warmup=20):
+    """Per-call latency of the four attention shapes that the Oxide Infer README's
+    Performance snapshot prints (HIP events around each launch, inputs resident,
+    so small working sets sit in cache, as in a serving loop).  Head counts are
+    not printed there: 32 q heads, 32 kv heads for MHA and 8 for GQA4."""
+    stream = torch.cuda.current_stream()
+    res = {}
+
+    def timed(name, call):
+        for i in range(warmup):
+            call(i)
+        t = LaunchTimer(torch, stream, iters)
+        t.run(call, iters)
+        ms = t.launch_ms(iters)
+        res[name] = {"us_median": round(float(np.median(ms)) * 1e3, 2),
+                     "us_mean": round(float(np.mean(ms)) * 1e3, 2)}
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(oxa.status_string(rc))
+
+    c = W.pages_decode_b1_kv1()
+    kv = c.kv
+    q = dev(c.q)
+    o = torch.empty_like(q)
+    args = (dev(kv.k_pool), dev(kv.v_pool), dev(kv.page_indptr), dev(kv.page_indices),
+            dev(kv.seq_lens))
+    timed("decode_mha_b1_kv1", lambda i: check(oxa.oxa_paged_decode(
+        q, *args, o, max_seq_len=1, sm_scale=c.sm_scale, layout=kv.layout,
+        num_kv_heads=kv.num_kv_heads)))
+
+    for name, rc_ in (("ragged_mha_q16_kv16", W.pages_ragged_mha_q16()),
+                      ("ragged_gqa4_q32+64_kv256+1024", W.pages_ragged_gqa4())):
+        qr, kr, vr = dev(rc_.q), dev(rc_.k), dev(rc_.v)
+        orr = torch.empty_like(qr)
+        qi, ki = dev(rc_.qo_indptr), dev(rc_.kv_indptr)
+        mq, mk = int(np.diff(rc_.qo_indptr).max()), int(np.diff(rc_.kv_indptr).max())
+        timed(name, lambda i, qr=qr, kr=kr, vr=vr, orr=orr, qi=qi, ki=ki, mq=mq, mk=mk, c=rc_:
+              check(oxa.oxa_ragged_prefill(qr, kr, vr, qi, ki, orr, max_qo_len=mq,
+                                           max_kv_len=mk, sm_scale=c.sm_scale, causal=True)))
+
+    pc = W.pages_paged_gqa4()
+    kv = pc.kv
+    qp = dev(pc.q)
+    op = torch.empty_like(qp)
+    pargs = (dev(pc.qo_indptr), dev(kv.k_pool), dev(kv.v_pool), dev(kv.page_indptr),
+             dev(kv.page_indices), dev(kv.seq_lens))
+    timed("paged_gqa4_q32+64_kv256+1024", lambda i: check(oxa.oxa_paged_prefill(
+        qp, *pargs, op, max_qo_len=64, max_seq_len=1024, sm_scale=pc.sm_scale,
+        layout=kv.layout, num_kv_heads=kv.num_kv_heads, causal=True)))
+    return res
+
+
 def cpu_baseline(case, budget_s=10.0):
     """The oracle's paged decode of the whole workload, repeated for ~budget_s,
     with its BLAS pool held to one thread."""
@@ -305,6 +359,10 @@ def main():
     if only in (None, "append", "prefill_paged"):
         log("append + paged prefill: 2 x 16384 tokens")
         out["long"] = bench_append_and_paged_prefill(torch, oxa, W.rope_append_prefill(), 10, 2)
+
+    if only in (None, "pages_shapes"):
+        log("pages_shapes: the four printed attention shapes, per-call latency")
+        out["pages_shapes"] = bench_pages_shapes(torch, oxa, W)
 
     if only == "copy":
         # a plain device copy of known size: the reference for scaling the HBM
@@ -395,6 +453,8 @@ def main():
                                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                         "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                                         "traffic": traffic, "kernel": "prefill_kernel"}}
+    if "pages_shapes" in out:
+        rows["pages_shapes_latency"] = out["pages_shapes"]
     line["rows"] = rows
     if "value" not in line:
         line.update({"value": None, "ms_per_step": None, "config": {"workload": only}})

@@ -20,6 +20,8 @@
 // K/V tiles are double-buffered: the next tile's loads are in flight during
 // the current tile's math.  Tiles are scheduled longest-first: the
 // query-tile index is the slowest grid dimension, counted from the end.
+#include <atomic>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -155,16 +157,29 @@ __device__ __forceinline__ int seq_tiles(const PrefillParams& p, int b) {
 }
 
 // In-place suffix sum over a[0 .. n) in LDS: a[t] <- a[t] + a[t+1] + ... .
+// Each thread owns a contiguous run of entries; the sum of all later runs
+// comes from a shuffle scan inside the wave plus the totals of later waves
+// (tot[0 .. kNW) holds those), so no thread walks a long serial chain of LDS
+// reads - the schedule is built at the start of every work-group, and on
+// short inputs it would otherwise cost more than the attention itself.
 __device__ __forceinline__ void lds_suffix_sum(int* a, int n, int* tot, int tid) {
   constexpr int kThreads = kNW * 64;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int per = (n + kThreads - 1) / kThreads;
   const int lo = min(tid * per, n), hi = min(lo + per, n);
   int sum = 0;
   for (int u = lo; u < hi; ++u) sum += a[u];
-  tot[tid] = sum;
+  int incl = sum;  // sum over lanes >= this one in the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_down(incl, off, 64);
+    if (lane + off < 64) incl += o;
+  }
+  if (lane == 0) tot[wave] = incl;
   __syncthreads();
-  int run = 0;
-  for (int u = tid + 1; u < kThreads; ++u) run += tot[u];
+  int run = incl - sum;
+  for (int w = wave + 1; w < kNW; ++w) run += tot[w];
   __syncthreads();
   for (int u = hi - 1; u >= lo; --u) {
     run += a[u];
@@ -479,6 +494,28 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
 
 }  // namespace
 
+// Compute units of the current device, queried once per device: the
+// attribute query walks the runtime's device properties and costs more host
+// time than a short prefill takes on the GPU.
+static hipError_t device_cu_count(int* cus) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return hipSuccess;
+    }
+  }
+  e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess && dev >= 0 && dev < kMaxDevices)
+    cached[dev].store(*cus, std::memory_order_relaxed);
+  return e;
+}
+
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream) {
   PrefillParams p;
   p.q = a.q;
@@ -510,9 +547,8 @@ hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream) {
   p.scale_log2 = a.sm_scale * kLog2e;
   // one persistent work-group per CU (a multiple of 8, so a kv head's items
   // stay on one XCD), never more than there can be items
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  int cus = 0;
+  hipError_t e = device_cu_count(&cus);
   if (e != hipSuccess) return e;
   const int64_t pairs_ub = ((int64_t)a.nnz_qo + p.bm - 1) / p.bm + a.batch;
   const int64_t items_ub = pairs_ub * p.hkv * p.head_tiles;

@@ -244,3 +244,51 @@ def rope_append_prefill(seq_len=16384, batch=2) -> AppendCase:
     whose pages and rotated q then feed a paged causal GQA4 prefill."""
     return append_case(1005, seq_lens=[seq_len] * batch, num_qo_heads=32, num_kv_heads=8,
                        sentinel=False)
+
+
+# ----------------------------------------------------------------------------
+# The attention shapes printed in the Oxide Infer README, Performance snapshot:
+# paged decode B1 / KV1, ragged prefill MHA Q16 / KV16, ragged and paged
+# prefill GQA4 with Q 32+64 over KV 256+1024; head dim 128, NHD, page size 16.
+# The pages print no head counts; these cases take 32 q heads (32 kv heads for
+# MHA, 8 for GQA4), as the other workloads do.
+
+PAGES_HQ = 32
+
+
+def pages_decode_b1_kv1(layout="NHD", poison=False) -> DecodeCase:
+    """Paged decode, MHA, one sequence holding a single key."""
+    return decode_case(1006, batch=1, num_qo_heads=PAGES_HQ, num_kv_heads=PAGES_HQ,
+                       seq_lens=[1], num_pages=4, layout=layout, poison=poison)
+
+
+def pages_ragged_mha_q16() -> RaggedCase:
+    """Ragged causal prefill, MHA, one sequence of 16 queries over 16 keys."""
+    return ragged_case(1007, qo_lens=[16], kv_lens=[16], num_qo_heads=PAGES_HQ,
+                       num_kv_heads=PAGES_HQ)
+
+
+def pages_ragged_gqa4() -> RaggedCase:
+    """Ragged causal prefill, GQA4: queries 32 + 64 at the end of keys 256 + 1024
+    (bottom-right causal alignment)."""
+    return ragged_case(1008, qo_lens=[32, 64], kv_lens=[256, 1024], num_qo_heads=PAGES_HQ,
+                       num_kv_heads=PAGES_HQ // 4)
+
+
+@dataclasses.dataclass
+class PagedPrefillCase:
+    q: np.ndarray               # uint16 [nnz_qo, Hq, 128]
+    qo_indptr: np.ndarray       # int32 [B + 1]
+    kv: PagedKV
+    num_qo_heads: int
+    sm_scale: float
+
+
+def pages_paged_gqa4(layout="NHD", poison=False) -> PagedPrefillCase:
+    """Paged causal prefill, GQA4: queries 32 + 64 over paged keys 256 + 1024."""
+    rng = np.random.default_rng(1009)
+    kv = make_paged_kv(rng, np.array([256, 1024], np.int32), PAGES_HQ // 4, layout=layout,
+                       poison=poison, extra_pages=0)
+    qo_indptr = indptr_from_counts([32, 64])
+    q = bf16_normal(rng, (int(qo_indptr[-1]), PAGES_HQ, HEAD_DIM))
+    return PagedPrefillCase(q, qo_indptr, kv, PAGES_HQ, 1.0 / math.sqrt(HEAD_DIM))
