@@ -195,9 +195,11 @@ def decode_partials(q_bits, k_pool, v_pool, layout, page_indptr, page_indices, s
 def merge_states(o_part, lse_part):
     """Combine partial attention states along the second-to-last axis of o_part.
 
-    lse = ln sum_p exp(lse_p);  o = sum_p exp(lse_p - lse) * o_p.  Partitions
-    with lse_p = -inf contribute nothing.  (The merge of the Single decode
-    split-K row; the "Attention state and cascade" domain's state merge.)
+    lse = ln sum_p exp(lse_p);  o = sum_p exp(lse_p - lse) * o_p.  A state with
+    lse_p = -inf (an empty key set) contributes nothing, whatever its o_p holds;
+    if every state is empty the result is (o = 0, lse = -inf).  (The merge of
+    the Single decode split-K row; the "Attention state and cascade" domain's
+    state merge.)
     """
     o_part = np.asarray(o_part, dtype=np.float64)
     lse_part = np.asarray(lse_part, dtype=np.float64)
@@ -205,9 +207,27 @@ def merge_states(o_part, lse_part):
     m_safe = np.where(np.isfinite(m), m, 0.0)
     w = np.exp(lse_part - m_safe)
     total = np.sum(w, axis=-1, keepdims=True)
-    lse = (m_safe + np.log(total))[..., 0]
-    o = np.sum((w / total)[..., None] * o_part, axis=-2)
+    with np.errstate(divide="ignore"):
+        lse = (m_safe + np.log(total))[..., 0]
+    live = ~np.isneginf(lse_part)
+    frac = np.where(live, w / np.where(total > 0, total, 1.0), 0.0)
+    o = np.sum(np.where(live[..., None], frac[..., None] * o_part, 0.0), axis=-2)
     return o, lse
+
+
+def merge_state_rows(v, lse):
+    """The state-merge operator over row-major states: v [R, S, H, D] and lse
+    [R, S, H] (S states of each (row, head)) -> v [R, H, D], lse [R, H]."""
+    v = np.asarray(v, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    return merge_states(np.transpose(v, (0, 2, 1, 3)), np.transpose(lse, (0, 2, 1)))
+
+
+def merge_state_pair(v_a, lse_a, v_b, lse_b):
+    """Two states of every (row, head): v [R, H, D], lse [R, H] each."""
+    v = np.stack([np.asarray(v_a, np.float64), np.asarray(v_b, np.float64)], axis=-2)
+    lse = np.stack([np.asarray(lse_a, np.float64), np.asarray(lse_b, np.float64)], axis=-1)
+    return merge_states(v, lse)
 
 
 # ---------------------------------------------------------------------------
