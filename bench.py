@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, TFLOP/s
 ROWS = ("decode", "decode_mha", "decode_mqa", "prefill_ragged", "append", "prefill_paged",
-        "pages_shapes", "copy")
+        "pages_shapes", "merge", "copy")
 
 
 def log(msg):
@@ -290,6 +290,51 @@ def bench_pages_shapes(torch, oxa, W, iters=200, warmup=20):
     return res
 
 
+def bench_merge(torch, oxa, iters=30, warmup=5):
+    """Attention-state merges at serving sizes, inputs cold (two copies rotate):
+    a cascade pair over 16384 rows x 32 heads (bf16 states, the prefill-batch
+    shape), and 8 f32 partial states over 512 rows x 32 heads into bf16."""
+    stream = torch.cuda.current_stream()
+    res = {}
+
+    def run(name, make, call, nbytes):
+        bufs = [make(i) for i in range(2)]
+        for i in range(warmup):
+            call(bufs[i % 2])
+        t = LaunchTimer(torch, stream, iters)
+        t.run(lambda i: call(bufs[i % 2]), iters)
+        ms = float(np.mean(t.launch_ms(iters)))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": nbytes}
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(oxa.status_string(rc))
+
+    R, H = 16384, 32
+    def make_pair(i):
+        g = torch.Generator(device="cuda").manual_seed(3000 + i)
+        va = torch.randn(R, H, 128, device="cuda", generator=g).to(torch.bfloat16)
+        vb = torch.randn(R, H, 128, device="cuda", generator=g).to(torch.bfloat16)
+        la = torch.randn(R, H, device="cuda", generator=g) * 4
+        lb = torch.randn(R, H, device="cuda", generator=g) * 4
+        return va, la, vb, lb, torch.empty_like(va), torch.empty_like(la)
+    run("merge_pair_bf16_r16384_h32", make_pair,
+        lambda b: check(oxa.oxa_merge_state_pair(*b)), R * H * (3 * 256 + 3 * 4))
+
+    R2, S2 = 512, 8
+    def make_multi(i):
+        g = torch.Generator(device="cuda").manual_seed(3100 + i)
+        v = torch.randn(R2, S2, H, 128, device="cuda", generator=g)
+        lse = torch.randn(R2, S2, H, device="cuda", generator=g) * 4
+        return v, lse, torch.empty(R2, H, 128, dtype=torch.bfloat16, device="cuda"), \
+            torch.empty(R2, H, device="cuda")
+    run("merge_f32x8_to_bf16_r512_h32", make_multi,
+        lambda b: check(oxa.oxa_merge_states(*b)), R2 * H * (S2 * (512 + 4) + 256 + 4))
+    return res
+
+
 def cpu_baseline(case, budget_s=10.0):
     """The oracle's paged decode of the whole workload, repeated for ~budget_s,
     with its BLAS pool held to one thread."""
@@ -363,6 +408,10 @@ def main():
     if only in (None, "pages_shapes"):
         log("pages_shapes: the four printed attention shapes, per-call latency")
         out["pages_shapes"] = bench_pages_shapes(torch, oxa, W)
+
+    if only in (None, "merge"):
+        log("merge: attention-state merges (cascade pair, 8 f32 partials)")
+        out["merge"] = bench_merge(torch, oxa)
 
     if only == "copy":
         # a plain device copy of known size: the reference for scaling the HBM
@@ -455,6 +504,8 @@ def main():
                                         "traffic": traffic, "kernel": "prefill_kernel"}}
     if "pages_shapes" in out:
         rows["pages_shapes_latency"] = out["pages_shapes"]
+    if "merge" in out:
+        rows.update(out["merge"])
     line["rows"] = rows
     if "value" not in line:
         line.update({"value": None, "ms_per_step": None, "config": {"workload": only}})

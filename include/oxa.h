@@ -11,6 +11,11 @@
  *   oxa_ragged_prefill     causal (or full) prefill over packed ragged K/V
  *   oxa_paged_prefill      causal (or full) prefill over paged K/V
  *
+ * and a standalone attention-state merge (oxa_merge_states,
+ * oxa_merge_state_pair) that combines the (output, lse) states of disjoint
+ * key sets, as split-K decode does internally and cascade / shared-prefix
+ * attention does across calls.
+ *
  * The operator contracts follow the "FlashInfer parity matrix" page (sections
  * "Admitted attention matrix", "Dispatch limits", "Paged KV ownership
  * difference", "Domain coverage") and the runtime rules on the "Oxide Infer"
@@ -67,17 +72,20 @@
 extern "C" {
 #endif
 
-#define OXA_ABI_VERSION 2
+#define OXA_ABI_VERSION 3
 #define OXA_PAGE_SIZE 16
 #define OXA_HEAD_DIM 128
 
 typedef enum { OXA_LAYOUT_NHD = 0, OXA_LAYOUT_HND = 1 } oxa_layout;
 
+/* element type of attention states (oxa_merge_*) */
+typedef enum { OXA_DTYPE_BF16 = 0, OXA_DTYPE_F32 = 1 } oxa_dtype;
+
 typedef enum {
   OXA_OK = 0,
   /* returned by the call itself; nothing was enqueued */
   OXA_ERR_NULL = 1,          /* a required pointer is NULL */
-  OXA_ERR_UNSUPPORTED = 2,   /* head_dim != 128, page_size != 16, unknown layout */
+  OXA_ERR_UNSUPPORTED = 2,   /* head_dim != 128, page_size != 16, unknown layout or dtype */
   OXA_ERR_SHAPE = 3,         /* a count or scalar is out of range, or Hq % Hkv != 0 */
   OXA_ERR_ALIGN = 4,         /* a bf16 tensor or the workspace is not 16-byte aligned */
   OXA_ERR_ALIAS = 5,         /* an output region overlaps an input or another output */
@@ -264,6 +272,53 @@ oxa_status oxa_paged_prefill(
 
 size_t oxa_paged_prefill_workspace_bytes(int32_t batch, int32_t nnz_qo, int32_t num_qo_heads,
                                          int32_t head_dim);
+
+/*
+ * Attention-state merge.  ("FlashInfer parity matrix": section Domain
+ * coverage, Attention state and cascade - the state merge; the merge of the
+ * Single decode split-K row of the Admitted attention matrix.)
+ *
+ * The state of one (row, head) over a set of keys is the softmax attention
+ * output v over that set ([128] values) and lse, the natural-log
+ * log-sum-exp of its scaled scores (f32).  States of disjoint key sets
+ * combine into the state of their union:
+ *     lse = ln sum_s exp(lse_s),     v = sum_s exp(lse_s - lse) * v_s
+ * in f32.  A state with lse_s = -inf (no keys) contributes nothing, whatever
+ * its v holds; if every state is empty, v = 0 and lse = -inf.  lse values
+ * must be finite or -inf (otherwise the result is unspecified).
+ *
+ * v_dtype is the type of the input states, out_dtype that of v_out
+ * (OXA_DTYPE_BF16 as uint16 bits, rounded to nearest even on output, or
+ * OXA_DTYPE_F32); lse_out (may be NULL) is f32.
+ *
+ * oxa_merge_states: S states per (row, head), stored row-major:
+ *   v   [num_rows][num_states][num_heads][128]   v_dtype
+ *   lse [num_rows][num_states][num_heads]        f32
+ *   v_out [num_rows][num_heads][128] out_dtype,  lse_out [num_rows][num_heads]
+ * Outputs may not overlap inputs.
+ *
+ * oxa_merge_state_pair: two states per (row, head) in separate tensors
+ *   v_a, v_b [num_rows][num_heads][128] v_dtype;  lse_a, lse_b [num_rows][num_heads]
+ *   v_out [num_rows][num_heads][128] out_dtype,   lse_out [num_rows][num_heads]
+ * In place: v_out may be exactly v_a or v_b (when out_dtype == v_dtype) and
+ * lse_out exactly lse_a or lse_b; any other overlap is rejected.
+ *
+ * Ranges: 0 <= num_rows (0 = no-op; the pointers may then be NULL),
+ * 1 <= num_states, 1 <= num_heads, head_dim == 128.  Alignment: v tensors 16
+ * bytes, lse tensors 4.  No workspace, no status: the merge has no
+ * data-dependent failure.
+ */
+oxa_status oxa_merge_states(
+    hipStream_t stream,
+    const void* v, const float* lse, int32_t v_dtype,
+    int32_t num_rows, int32_t num_states, int32_t num_heads, int32_t head_dim,
+    void* v_out, int32_t out_dtype, float* lse_out);
+
+oxa_status oxa_merge_state_pair(
+    hipStream_t stream,
+    const void* v_a, const float* lse_a, const void* v_b, const float* lse_b, int32_t v_dtype,
+    int32_t num_rows, int32_t num_heads, int32_t head_dim,
+    void* v_out, int32_t out_dtype, float* lse_out);
 
 #ifdef __cplusplus
 }

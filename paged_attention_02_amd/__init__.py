@@ -38,6 +38,8 @@ OXA_DEV_CAPACITY = 21
 OXA_DEV_BATCH_INDEX = 22
 
 LAYOUTS = {"NHD": 0, "HND": 1}
+OXA_DTYPE_BF16 = 0
+OXA_DTYPE_F32 = 1
 PAGE_SIZE = 16
 HEAD_DIM = 128
 
@@ -61,6 +63,8 @@ SIGNATURES = {
     "oxa_paged_prefill": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _I, _P, _I, _I, _I, _I, _I,
                                _I, _I, _I, _F, _P, _Z, _P, _P, _P]),
     "oxa_paged_prefill_workspace_bytes": (_Z, [_I, _I, _I, _I]),
+    "oxa_merge_states": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P]),
+    "oxa_merge_state_pair": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P]),
 }
 
 _lib = None
@@ -132,6 +136,21 @@ def _f32(t, name):
     if t is not None and t.dtype != torch.float32:
         raise TypeError(f"{name} must be float32")
     return _ptr(t)
+
+
+def _state_dtype(t, name) -> int:
+    """oxa_dtype of an attention-state tensor: bf16 (or its bits) or float32."""
+    import torch
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return OXA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return OXA_DTYPE_F32
+    raise TypeError(f"{name} must be bf16 or float32")
+
+
+def _shape(t, shape, name):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
 def _stream(stream) -> int:
@@ -227,3 +246,33 @@ def oxa_paged_prefill(q, qo_indptr, k_pages, v_pages, page_indptr, page_indices,
         q.shape[1], num_kv_heads, q.shape[2], int(max_qo_len), int(max_seq_len),
         int(bool(causal)), float(sm_scale), None, 0, _bf16(o, "o"), _f32(lse, "lse"),
         _i32(status, "status"))
+
+
+def oxa_merge_states(v, lse, v_out, lse_out=None, *, stream=None) -> int:
+    """Merge S attention states per (row, head): v [R, S, H, 128] (bf16 or f32),
+    lse [R, S, H] f32 -> v_out [R, H, 128] (bf16 or f32), lse_out [R, H] f32."""
+    R, S, H, D = v.shape
+    _shape(lse, (R, S, H), "lse")
+    _shape(v_out, (R, H, D), "v_out")
+    _shape(lse_out, (R, H), "lse_out")
+    return lib().oxa_merge_states(
+        _stream(stream), _ptr(v), _f32(lse, "lse"), _state_dtype(v, "v"), R, S, H, D, _ptr(v_out),
+        _state_dtype(v_out, "v_out"), _f32(lse_out, "lse_out"))
+
+
+def oxa_merge_state_pair(v_a, lse_a, v_b, lse_b, v_out, lse_out=None, *, stream=None) -> int:
+    """Merge two attention states per (row, head): v_a, v_b [R, H, 128] (same
+    dtype), lse_a, lse_b [R, H] f32 -> v_out [R, H, 128], lse_out [R, H]; v_out
+    may be v_a or v_b itself (and lse_out lse_a or lse_b) for an in-place merge."""
+    R, H, D = v_a.shape
+    if v_b.dtype != v_a.dtype:
+        raise TypeError("v_a and v_b must have the same dtype")
+    _shape(v_b, (R, H, D), "v_b")
+    _shape(lse_a, (R, H), "lse_a")
+    _shape(lse_b, (R, H), "lse_b")
+    _shape(v_out, (R, H, D), "v_out")
+    _shape(lse_out, (R, H), "lse_out")
+    return lib().oxa_merge_state_pair(
+        _stream(stream), _ptr(v_a), _f32(lse_a, "lse_a"), _ptr(v_b), _f32(lse_b, "lse_b"),
+        _state_dtype(v_a, "v_a"), R, H, D, _ptr(v_out), _state_dtype(v_out, "v_out"),
+        _f32(lse_out, "lse_out"))

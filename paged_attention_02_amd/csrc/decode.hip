@@ -370,46 +370,6 @@ void paged_decode_kernel(DecodeParams p) {
   }
 }
 
-// LSE merge of split-K partial states: one 128-thread group per (sequence,
-// q head), thread d owns output dim d.  One pass with a running maximum over
-// chunks of 8 partitions, whose loads are issued together.
-__global__ __launch_bounds__(128) void merge_partials_kernel(const float* ws_o, const float* ws_lse,
-                                                             int num_partitions, uint16_t* o,
-                                                             float* lse) {
-  constexpr int kChunk = 8;
-  const int64_t row = blockIdx.x;
-  const int d = threadIdx.x;
-  const float* lp = ws_lse + row * num_partitions;
-  const float* op = ws_o + row * num_partitions * kHeadDim + d;
-  float mx = -INFINITY, wsum = 0.f, acc = 0.f;
-  for (int i0 = 0; i0 < num_partitions; i0 += kChunk) {
-    float w[kChunk], v[kChunk];
-#pragma unroll
-    for (int j = 0; j < kChunk; ++j) {
-      const bool in = i0 + j < num_partitions;
-      w[j] = in ? lp[i0 + j] : -INFINITY;
-      v[j] = in ? op[(int64_t)(i0 + j) * kHeadDim] : 0.f;
-    }
-    float cm = mx;
-#pragma unroll
-    for (int j = 0; j < kChunk; ++j) cm = fmaxf(cm, w[j]);
-    if (cm == -INFINITY) continue;  // nothing live yet
-    const float r = __expf(mx - cm);  // 0 while mx is -inf
-    wsum *= r;
-    acc *= r;
-#pragma unroll
-    for (int j = 0; j < kChunk; ++j) {
-      const float e = __expf(w[j] - cm);
-      wsum += e;
-      acc += e * v[j];
-    }
-    mx = cm;
-  }
-  const float val = wsum > 0.f ? acc / wsum : 0.f;
-  o[row * kHeadDim + d] = (uint16_t)(pack_bf16x2(val, 0.f) & 0xffffu);
-  if (d == 0 && lse != nullptr) lse[row] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
-}
-
 template <int LAYOUT>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
   const size_t stage = (size_t)kPidWin * 4 + (size_t)kNW * 2 * kStageBytes;
@@ -451,9 +411,25 @@ hipError_t launch_paged_decode(const DecodeLaunch& a, hipStream_t stream) {
   p.scale_log2 = a.sm_scale * kLog2e;
   hipError_t e = a.layout == 0 ? launch_decode_t<0>(p, stream) : launch_decode_t<1>(p, stream);
   if (e != hipSuccess || a.num_partitions == 1) return e;
-  hipLaunchKernelGGL(merge_partials_kernel, dim3(a.batch * a.hq), dim3(kHeadDim), 0, stream,
-                     a.ws_o, a.ws_lse, a.num_partitions, a.o, a.lse);
-  return hipGetLastError();
+  // merge the partitions: workspace [batch][hq][P][128] f32 -> o bf16
+  MergeLaunch m = {};
+  m.v[0] = a.ws_o;
+  m.lse[0] = a.ws_lse;
+  m.v_row = (int64_t)a.hq * a.num_partitions * kHeadDim;
+  m.v_head = (int64_t)a.num_partitions * kHeadDim;
+  m.v_state = kHeadDim;
+  m.l_row = (int64_t)a.hq * a.num_partitions;
+  m.l_head = a.num_partitions;
+  m.l_state = 1;
+  m.units = (int64_t)a.batch * a.hq;
+  m.heads = a.hq;
+  m.states = a.num_partitions;
+  m.in_f32 = 1;
+  m.out_f32 = 0;
+  m.pair = 0;
+  m.out = a.o;
+  m.lse_out = a.lse;
+  return launch_merge_states(m, stream);
 }
 
 }  // namespace oxa

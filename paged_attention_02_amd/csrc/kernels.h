@@ -64,4 +64,23 @@ struct PrefillLaunch {
 };
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream);
 
+// Attention-state merge over (row, head) units.  State s of unit (row, h)
+// has its 128 values at element offset row * v_row + h * v_head + s * v_state
+// of v[0] (or at row * v_row + h * v_head of v[s] for a pair), and its lse at
+// row * l_row + h * l_head + s * l_state of lse[0] (lse[s] for a pair).
+// Outputs are contiguous: out [units][128], lse_out [units] (may be null).
+struct MergeLaunch {
+  const void* v[2];
+  const float* lse[2];
+  int64_t v_row, v_head, v_state;
+  int64_t l_row, l_head, l_state;
+  int64_t units;  // rows * heads
+  int32_t heads, states, in_f32, out_f32, pair;
+  void* out;
+  float* lse_out;
+};
+hipError_t launch_merge_states(const MergeLaunch& a, hipStream_t stream);
+// Work-groups launch_merge_states uses for `units` units.
+int64_t merge_states_groups(int64_t units, int in_f32);
+
 }  // namespace oxa

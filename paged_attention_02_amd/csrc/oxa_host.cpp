@@ -63,6 +63,21 @@ oxa_status check_paging(int32_t page_size, int32_t layout, int32_t num_pages,
 
 oxa_status launch_status(hipError_t e) { return e == hipSuccess ? OXA_OK : OXA_ERR_LAUNCH; }
 
+bool dtype_ok(int32_t t) { return t == OXA_DTYPE_BF16 || t == OXA_DTYPE_F32; }
+uint64_t dtype_bytes(int32_t t) { return t == OXA_DTYPE_F32 ? 4 : 2; }
+
+// The merge kernels use one work-group per few (row, head) units.
+oxa_status check_merge_shape(int32_t num_rows, int32_t num_states, int32_t num_heads,
+                             int32_t head_dim, int32_t v_dtype, int32_t out_dtype) {
+  if (head_dim != OXA_HEAD_DIM || !dtype_ok(v_dtype) || !dtype_ok(out_dtype))
+    return OXA_ERR_UNSUPPORTED;
+  if (num_rows < 0 || num_states < 1 || num_heads < 1) return OXA_ERR_SHAPE;
+  const int64_t units = (int64_t)num_rows * num_heads;
+  if (oxa::merge_states_groups(units, v_dtype == OXA_DTYPE_F32) > 0x7fffffffll)
+    return OXA_ERR_SHAPE;
+  return OXA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -392,6 +407,92 @@ oxa_status oxa_paged_prefill(hipStream_t stream, const uint16_t* q, const int32_
   a.num_page_entries = num_page_entries;
   a.sm_scale = sm_scale;
   return launch_status(oxa::launch_prefill(a, stream));
+}
+
+// ---------------------------------------------------------------- state merge
+
+oxa_status oxa_merge_states(hipStream_t stream, const void* v, const float* lse, int32_t v_dtype,
+                            int32_t num_rows, int32_t num_states, int32_t num_heads,
+                            int32_t head_dim, void* v_out, int32_t out_dtype, float* lse_out) {
+  if (num_rows != 0 && (!v || !lse || !v_out)) return OXA_ERR_NULL;
+  if (oxa_status s = check_merge_shape(num_rows, num_states, num_heads, head_dim, v_dtype,
+                                       out_dtype))
+    return s;
+  if (num_rows == 0) return OXA_OK;
+  if (!aligned(v, 16) || !aligned(v_out, 16) || !aligned(lse, 4) || !aligned(lse_out, 4))
+    return OXA_ERR_ALIGN;
+  const uint64_t units = (uint64_t)num_rows * num_heads;
+  const Region ins[] = {{v, units * num_states * OXA_HEAD_DIM * dtype_bytes(v_dtype)},
+                        {lse, units * num_states * 4}};
+  const Region outs[] = {{v_out, units * OXA_HEAD_DIM * dtype_bytes(out_dtype)},
+                         {lse_out, lse_out ? units * 4 : 0}};
+  if (any_alias(outs, 2, ins, 2)) return OXA_ERR_ALIAS;
+
+  oxa::MergeLaunch m = {};
+  m.v[0] = v;
+  m.lse[0] = lse;
+  m.v_row = (int64_t)num_states * num_heads * OXA_HEAD_DIM;
+  m.v_head = OXA_HEAD_DIM;
+  m.v_state = (int64_t)num_heads * OXA_HEAD_DIM;
+  m.l_row = (int64_t)num_states * num_heads;
+  m.l_head = 1;
+  m.l_state = num_heads;
+  m.units = (int64_t)units;
+  m.heads = num_heads;
+  m.states = num_states;
+  m.in_f32 = v_dtype == OXA_DTYPE_F32;
+  m.out_f32 = out_dtype == OXA_DTYPE_F32;
+  m.pair = 0;
+  m.out = v_out;
+  m.lse_out = lse_out;
+  return launch_status(oxa::launch_merge_states(m, stream));
+}
+
+oxa_status oxa_merge_state_pair(hipStream_t stream, const void* v_a, const float* lse_a,
+                                const void* v_b, const float* lse_b, int32_t v_dtype,
+                                int32_t num_rows, int32_t num_heads, int32_t head_dim,
+                                void* v_out, int32_t out_dtype, float* lse_out) {
+  if (num_rows != 0 && (!v_a || !lse_a || !v_b || !lse_b || !v_out)) return OXA_ERR_NULL;
+  if (oxa_status s = check_merge_shape(num_rows, 2, num_heads, head_dim, v_dtype, out_dtype))
+    return s;
+  if (num_rows == 0) return OXA_OK;
+  if (!aligned(v_a, 16) || !aligned(v_b, 16) || !aligned(v_out, 16) || !aligned(lse_a, 4) ||
+      !aligned(lse_b, 4) || !aligned(lse_out, 4))
+    return OXA_ERR_ALIGN;
+  const uint64_t units = (uint64_t)num_rows * num_heads;
+  const uint64_t vin = units * OXA_HEAD_DIM * dtype_bytes(v_dtype);
+  const uint64_t vout = units * OXA_HEAD_DIM * dtype_bytes(out_dtype);
+  // exact aliasing of an output with one input is the in-place form: each
+  // (row, head) reads its inputs before it writes the same places
+  const bool v_in_place = out_dtype == v_dtype && (v_out == v_a || v_out == v_b);
+  const bool l_in_place = lse_out != nullptr && (lse_out == lse_a || lse_out == lse_b);
+  const Region vo{v_out, vout};
+  const Region lo{lse_out, lse_out ? units * 4 : 0};
+  const Region va{v_a, vin}, vb{v_b, vin}, la{lse_a, units * 4}, lb{lse_b, units * 4};
+  if (overlaps(vo, lo) || overlaps(vo, la) || overlaps(vo, lb) || overlaps(lo, va) ||
+      overlaps(lo, vb))
+    return OXA_ERR_ALIAS;
+  if (!v_in_place && (overlaps(vo, va) || overlaps(vo, vb))) return OXA_ERR_ALIAS;
+  if (!l_in_place && (overlaps(lo, la) || overlaps(lo, lb))) return OXA_ERR_ALIAS;
+
+  oxa::MergeLaunch m = {};
+  m.v[0] = v_a;
+  m.v[1] = v_b;
+  m.lse[0] = lse_a;
+  m.lse[1] = lse_b;
+  m.v_row = (int64_t)num_heads * OXA_HEAD_DIM;
+  m.v_head = OXA_HEAD_DIM;
+  m.l_row = num_heads;
+  m.l_head = 1;
+  m.units = (int64_t)units;
+  m.heads = num_heads;
+  m.states = 2;
+  m.in_f32 = v_dtype == OXA_DTYPE_F32;
+  m.out_f32 = out_dtype == OXA_DTYPE_F32;
+  m.pair = 1;
+  m.out = v_out;
+  m.lse_out = lse_out;
+  return launch_status(oxa::launch_merge_states(m, stream));
 }
 
 }  // extern "C"

@@ -1,0 +1,174 @@
+"""Attention-state merge on the GPU vs the FP64 oracle.
+
+oxa_merge_states over row-major [R, S, H, 128] states in every input/output
+dtype pair (empty states carry NaN values that must not leak; one (row, head)
+has no live state at all), oxa_merge_state_pair out of place and in place,
+a cascade (paged decode over a prefix and over the rest of each sequence,
+merged) against the oracle's decode over the whole sequence, and a large
+merge compared in full.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import attention as A
+from oracle import bf16
+from tests.gpu_helpers import assert_attention_close, assert_lse_close, dev, host, host_bits, note
+from tests.lib_loader import ensure_built
+
+import paged_attention_02_amd as oxa
+
+pytestmark = pytest.mark.gpu
+
+# f32 outputs: the merge's only rounding is f32 arithmetic (exp2 of the
+# base-2 scaled lse differences, a short weighted sum, one reciprocal):
+# a few 1e-7 relative per term on values of order 1.
+F32_RTOL = 1e-5
+F32_ATOL = 1e-5
+
+
+def _f64(v, dtype):
+    return bf16.to_f64(v) if dtype == "bf16" else np.asarray(v, np.float64)
+
+
+def _out(shape, dtype):
+    return torch.empty(shape, dtype=torch.int16 if dtype == "bf16" else torch.float32,
+                       device="cuda")
+
+
+def _check(got_t, ref, dtype, what):
+    if dtype == "bf16":
+        assert_attention_close(host_bits(got_t), ref, what)
+    else:
+        np.testing.assert_allclose(host(got_t), ref, rtol=F32_RTOL, atol=F32_ATOL, err_msg=what)
+
+
+@pytest.mark.parametrize("din,dout", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "bf16"),
+                                      ("f32", "f32")])
+@pytest.mark.parametrize("R,S,H", [(37, 5, 6), (9, 19, 3), (1, 1, 1), (3, 8, 32)])
+def test_merge_states_vs_oracle(din, dout, R, S, H):
+    case = W.merge_case(2000 + R + S + H, R, S, H, dtype=din)
+    ensure_built()
+    v = dev(case.v)
+    lse = dev(case.lse)
+    o = _out((R, H, 128), dout)
+    lo = torch.empty(R, H, dtype=torch.float32, device="cuda")
+    note(f"merge_states R={R} S={S} H={H} {din}->{dout}")
+    assert oxa.oxa_merge_states(v, lse, o, lo) == oxa.OXA_OK
+    torch.cuda.synchronize()
+    o_ref, lse_ref = A.merge_state_rows(_f64(case.v, din), case.lse)
+    _check(o, o_ref, dout, f"merge {din}->{dout}")
+    got_l = host(lo)
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(lse_ref))
+    assert_lse_close(got_l, lse_ref)
+    # the unit with no live state: zeros and -inf
+    assert not host(o)[0, 0].any() and np.isneginf(got_l[0, 0])
+
+
+def test_merge_states_without_lse_out_and_with_no_rows():
+    case = W.merge_case(2100, 11, 3, 4)
+    ensure_built()
+    o = _out((11, 4, 128), "bf16")
+    assert oxa.oxa_merge_states(dev(case.v), dev(case.lse), o) == oxa.OXA_OK
+    torch.cuda.synchronize()
+    o_ref, _ = A.merge_state_rows(bf16.to_f64(case.v), case.lse)
+    assert_attention_close(host_bits(o), o_ref, "no lse_out")
+    empty_v = torch.empty(0, 3, 4, 128, dtype=torch.int16, device="cuda")
+    empty_l = torch.empty(0, 3, 4, dtype=torch.float32, device="cuda")
+    empty_o = torch.empty(0, 4, 128, dtype=torch.int16, device="cuda")
+    assert oxa.oxa_merge_states(empty_v, empty_l, empty_o) == oxa.OXA_OK
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_merge_state_pair_out_of_place_and_in_place(dtype):
+    R, H = 50, 8
+    case = W.merge_case(2200, R, 2, H, dtype=dtype)
+    ensure_built()
+    va, vb = dev(case.v[:, 0]), dev(case.v[:, 1])
+    la, lb = dev(case.lse[:, 0]), dev(case.lse[:, 1])
+    o = _out((R, H, 128), dtype)
+    lo = torch.empty(R, H, dtype=torch.float32, device="cuda")
+    note(f"merge_state_pair {dtype}")
+    assert oxa.oxa_merge_state_pair(va, la, vb, lb, o, lo) == oxa.OXA_OK
+    torch.cuda.synchronize()
+    o_ref, lse_ref = A.merge_state_pair(_f64(case.v[:, 0], dtype), case.lse[:, 0],
+                                        _f64(case.v[:, 1], dtype), case.lse[:, 1])
+    _check(o, o_ref, dtype, f"pair {dtype}")
+    assert_lse_close(host(lo), lse_ref)
+    # in place into a, then (from fresh copies) into b: the same bits
+    va2, la2 = va.clone(), la.clone()
+    assert oxa.oxa_merge_state_pair(va2, la2, vb, lb, va2, la2) == oxa.OXA_OK
+    vb3, lb3 = vb.clone(), lb.clone()
+    assert oxa.oxa_merge_state_pair(va, la, vb3, lb3, vb3, lb3) == oxa.OXA_OK
+    torch.cuda.synchronize()
+    for got_v, got_l in ((va2, la2), (vb3, lb3)):
+        assert torch.equal(got_v, o) and torch.equal(got_l, lo)
+
+
+@pytest.mark.parametrize("dout", ["bf16", "f32"])
+def test_cascade_prefix_and_suffix_decode_merge_to_the_whole(dout):
+    """Decode each sequence's first pages and its remaining pages as two
+    separate paged decodes, merge the two states, and compare with the oracle's
+    decode over the whole sequence (a shared-prefix cascade)."""
+    rng = np.random.default_rng(2300)
+    lens = np.array([300, 17, 1000, 64], np.int32)
+    hq, hkv = 32, 8
+    kv = W.make_paged_kv(rng, lens, hkv, poison=True)
+    q = W.bf16_normal(rng, (len(lens), hq, 128))
+    scale = 1.0 / np.sqrt(128.0)
+    pages = np.diff(kv.page_indptr)
+    pre_pages = np.maximum(1, pages // 3)
+    pre_pages = np.minimum(pre_pages, pages - 1)
+    pre_lens = (pre_pages * 16).astype(np.int32)
+    suf_lens = (lens - pre_lens).astype(np.int32)
+    assert (pre_lens >= 16).all() and (suf_lens >= 1).all()
+    pre_ids = np.concatenate([kv.page_indices[kv.page_indptr[b]:kv.page_indptr[b] + pre_pages[b]]
+                              for b in range(len(lens))]).astype(np.int32)
+    suf_ids = np.concatenate([kv.page_indices[kv.page_indptr[b] + pre_pages[b]:kv.page_indptr[b + 1]]
+                              for b in range(len(lens))]).astype(np.int32)
+    pre_ptr = W.indptr_from_counts(pre_pages)
+    suf_ptr = W.indptr_from_counts(pages - pre_pages)
+    ensure_built()
+    kp, vp, qd = dev(kv.k_pool), dev(kv.v_pool), dev(q)
+    states = []
+    for ptr, ids, sl in ((pre_ptr, pre_ids, pre_lens), (suf_ptr, suf_ids, suf_lens)):
+        o = torch.empty_like(qd)
+        lse = torch.empty(len(lens), hq, dtype=torch.float32, device="cuda")
+        note(f"cascade decode lens={sl.tolist()}")
+        rc = oxa.oxa_paged_decode(qd, kp, vp, dev(ptr), dev(ids), dev(sl), o,
+                                  max_seq_len=int(sl.max()), sm_scale=scale, num_kv_heads=hkv,
+                                  lse=lse)
+        assert rc == oxa.OXA_OK
+        states.append((o, lse))
+    om = _out((len(lens), hq, 128), dout)
+    lm = torch.empty(len(lens), hq, dtype=torch.float32, device="cuda")
+    assert oxa.oxa_merge_state_pair(states[0][0], states[0][1], states[1][0], states[1][1], om,
+                                    lm) == oxa.OXA_OK
+    torch.cuda.synchronize()
+    o_ref, lse_ref = A.paged_decode(q, kv.k_pool, kv.v_pool, "NHD", kv.page_indptr,
+                                    kv.page_indices, lens, scale)
+    if dout == "bf16":
+        assert_attention_close(host_bits(om), o_ref, "cascade")
+    else:
+        # bf16 partial states: their rounding bounds the error, not the merge
+        got = host(om)
+        err = got - o_ref
+        assert np.max(np.abs(err)) <= 2e-2
+        assert np.linalg.norm(err) / np.linalg.norm(o_ref) <= 5e-3
+    assert_lse_close(host(lm), lse_ref)
+
+
+def test_large_merge_in_full():
+    """2048 rows x 4 states x 32 heads (bf16 in, bf16 out): every element."""
+    R, S, H = 2048, 4, 32
+    case = W.merge_case(2400, R, S, H, dtype="bf16", empty_frac=0.1, all_empty_units=3)
+    ensure_built()
+    o = _out((R, H, 128), "bf16")
+    lo = torch.empty(R, H, dtype=torch.float32, device="cuda")
+    note(f"merge_states large R={R} S={S} H={H}")
+    assert oxa.oxa_merge_states(dev(case.v), dev(case.lse), o, lo) == oxa.OXA_OK
+    torch.cuda.synchronize()
+    o_ref, lse_ref = A.merge_state_rows(bf16.to_f64(case.v), case.lse)
+    assert_attention_close(host_bits(o), o_ref, "large merge")
+    assert_lse_close(host(lo), lse_ref)

@@ -142,3 +142,63 @@ def call_append(**over):
 ])
 def test_append_rejections(over, code):
     assert call_append(**over) == code
+
+
+def call_merge(**over):
+    args = dict(stream=None, v=addr(0), lse=addr(1), v_dtype=0, rows=4, states=3, heads=8,
+                head_dim=128, v_out=addr(2), out_dtype=0, lse_out=addr(3))
+    args.update(over)
+    return ensure_built().oxa_merge_states(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(v=None), oxa.OXA_ERR_NULL),
+    (dict(lse=None), oxa.OXA_ERR_NULL),
+    (dict(v_out=None), oxa.OXA_ERR_NULL),
+    (dict(head_dim=64), oxa.OXA_ERR_UNSUPPORTED),
+    (dict(v_dtype=2), oxa.OXA_ERR_UNSUPPORTED),
+    (dict(out_dtype=-1), oxa.OXA_ERR_UNSUPPORTED),
+    (dict(rows=-1), oxa.OXA_ERR_SHAPE),
+    (dict(states=0), oxa.OXA_ERR_SHAPE),
+    (dict(heads=0), oxa.OXA_ERR_SHAPE),
+    (dict(v=addr(0) + 8), oxa.OXA_ERR_ALIGN),
+    (dict(v_out=addr(2) + 4), oxa.OXA_ERR_ALIGN),
+    (dict(lse_out=addr(3) + 2), oxa.OXA_ERR_ALIGN),
+    (dict(v_out=addr(0) + 1024), oxa.OXA_ERR_ALIAS),    # output inside the states
+    (dict(lse_out=addr(1) + 16), oxa.OXA_ERR_ALIAS),    # lse_out inside lse
+    (dict(lse_out=addr(2) + 256), oxa.OXA_ERR_ALIAS),   # lse_out inside v_out
+    (dict(v_out=addr(0)), oxa.OXA_ERR_ALIAS),           # no in-place form for S states
+])
+def test_merge_states_rejections(over, code):
+    assert call_merge(**over) == code
+
+
+def test_merge_with_no_rows_is_a_no_op():
+    # nothing to merge: accepted without pointers, nothing enqueued
+    assert call_merge(rows=0, v=None, lse=None, v_out=None, lse_out=None) == oxa.OXA_OK
+
+
+def call_pair(**over):
+    args = dict(stream=None, v_a=addr(0), lse_a=addr(1), v_b=addr(2), lse_b=addr(3), v_dtype=0,
+                rows=4, heads=8, head_dim=128, v_out=addr(4), out_dtype=0, lse_out=addr(5))
+    args.update(over)
+    return ensure_built().oxa_merge_state_pair(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(v_b=None), oxa.OXA_ERR_NULL),
+    (dict(lse_b=None), oxa.OXA_ERR_NULL),
+    (dict(head_dim=256), oxa.OXA_ERR_UNSUPPORTED),
+    (dict(v_dtype=7), oxa.OXA_ERR_UNSUPPORTED),
+    (dict(rows=-2), oxa.OXA_ERR_SHAPE),
+    (dict(heads=0), oxa.OXA_ERR_SHAPE),
+    (dict(v_b=addr(2) + 2), oxa.OXA_ERR_ALIGN),
+    (dict(lse_a=addr(1) + 1), oxa.OXA_ERR_ALIGN),
+    (dict(v_out=addr(0) + 256), oxa.OXA_ERR_ALIAS),     # partial overlap with v_a
+    (dict(v_out=addr(0), out_dtype=1), oxa.OXA_ERR_ALIAS),  # in place needs one dtype
+    (dict(lse_out=addr(1) + 4), oxa.OXA_ERR_ALIAS),     # shifted onto lse_a
+    (dict(lse_out=addr(2)), oxa.OXA_ERR_ALIAS),         # lse_out over v_b
+    (dict(v_out=addr(3)), oxa.OXA_ERR_ALIAS),           # v_out over lse_b
+])
+def test_merge_state_pair_rejections(over, code):
+    assert call_pair(**over) == code

@@ -292,3 +292,34 @@ def pages_paged_gqa4(layout="NHD", poison=False) -> PagedPrefillCase:
     qo_indptr = indptr_from_counts([32, 64])
     q = bf16_normal(rng, (int(qo_indptr[-1]), PAGES_HQ, HEAD_DIM))
     return PagedPrefillCase(q, qo_indptr, kv, PAGES_HQ, 1.0 / math.sqrt(HEAD_DIM))
+
+
+# ----------------------------------------------------------------------------
+# Attention states for the state merge: random outputs and log-sum-exps (not
+# the states of any real attention; the merge is defined for any such input).
+
+@dataclasses.dataclass
+class MergeCase:
+    v: np.ndarray        # [R, S, H, 128]: uint16 bf16 bits, or float32
+    lse: np.ndarray      # float32 [R, S, H]; -inf marks an empty state
+    dtype: str           # "bf16" or "f32"
+
+
+def merge_case(seed, rows, states, heads, dtype="bf16", empty_frac=0.2, all_empty_units=1,
+               lse_scale=4.0) -> MergeCase:
+    """States v ~ N(0, 1) (bf16 or f32), lse ~ N(0, lse_scale^2); a fraction of
+    the states are empty (lse = -inf, v NaN) and the first ``all_empty_units``
+    (row, head) units have no live state at all."""
+    rng = np.random.default_rng(seed)
+    shape = (rows, states, heads, HEAD_DIM)
+    if dtype == "bf16":
+        v = bf16_normal(rng, shape)
+    else:
+        v = rng.standard_normal(size=shape, dtype=np.float32)
+    lse = (rng.standard_normal(size=(rows, states, heads)) * lse_scale).astype(np.float32)
+    empty = rng.random((rows, states, heads)) < empty_frac
+    for u in range(min(all_empty_units, rows * heads)):
+        empty[u // heads, :, u % heads] = True
+    lse[empty] = -np.inf
+    v[empty] = NAN_BITS if dtype == "bf16" else np.float32(np.nan)
+    return MergeCase(v, lse, dtype)
