@@ -251,8 +251,25 @@ def bench_pages_shapes(torch, oxa, W, iters=200, warmup=20):
         t = LaunchTimer(torch, stream, iters)
         t.run(call, iters)
         ms = t.launch_ms(iters)
+        # the same call captured once in a HIP graph and replayed
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            call(0)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call(0)
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            g.replay()
+        tg = LaunchTimer(torch, stream, iters)
+        tg.run(lambda i: g.replay(), iters)
+        gms = tg.launch_ms(iters)
         res[name] = {"us_median": round(float(np.median(ms)) * 1e3, 2),
-                     "us_mean": round(float(np.mean(ms)) * 1e3, 2)}
+                     "us_mean": round(float(np.mean(ms)) * 1e3, 2),
+                     "graph_us_median": round(float(np.median(gms)) * 1e3, 2)}
 
     def check(rc):
         if rc != 0:
