@@ -20,6 +20,16 @@ Readings of points the pages leave open:
 * The fused op also rotates Q when a Q tensor is given (rotated Q is what the
   following prefill reads); V is stored unrotated.
 * Rotation happens in float64 from the bf16 inputs and is rounded to bf16 once.
+* Standalone RoPE (the Standard RoPE row) rotates q and k of each token at its
+  explicit position; any int32 position is allowed (a negative one rotates
+  backwards).
+* The Llama 3.1 variant ("Domain coverage", RoPE: standard, Llama 3.1 and
+  fused variants; the pages name it and give no formula) is taken as the
+  published Llama 3.1 frequency rule: with the standard table f_i and
+  wavelength w_i = 2 pi / f_i, frequencies whose wavelength is shorter than
+  original_max_position / high_freq_factor stay, those longer than
+  original_max_position / low_freq_factor are divided by factor, and those in
+  between blend the two linearly in original_max_position / w_i.
 * A call whose tokens break any rule writes nothing (all or nothing) and
   reports the first failing token's reason, checking per token in this order:
   "batch_index" (0 <= b < batch), "capacity" (0 <= pos < 16 * pages listed for
@@ -41,22 +51,38 @@ def inv_freq(theta, head_dim):
     return np.float64(theta) ** (-2.0 * i / head_dim)
 
 
-def rope_neox(x, positions, theta):
-    """Rotate float64 x [..., D] at integer positions [...] (NeoX split-half)."""
+def inv_freq_llama31(theta, head_dim, factor, low_freq_factor, high_freq_factor,
+                     original_max_position):
+    """The Llama 3.1 rescaling of the standard frequency table, float64."""
+    base = inv_freq(theta, head_dim)
+    wavelen = 2.0 * np.pi / base
+    low_freq_wavelen = original_max_position / low_freq_factor
+    high_freq_wavelen = original_max_position / high_freq_factor
+    smooth = (original_max_position / wavelen - low_freq_factor) / (
+        high_freq_factor - low_freq_factor)
+    blended = (1.0 - smooth) * base / factor + smooth * base
+    out = np.where(wavelen > low_freq_wavelen, base / factor, blended)
+    return np.where(wavelen < high_freq_wavelen, base, out)
+
+
+def rope_neox(x, positions, theta, freqs=None):
+    """Rotate float64 x [..., D] at integer positions [...] (NeoX split-half),
+    with the standard table for theta or the given table ``freqs`` [D/2]."""
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
     half = d // 2
-    angle = np.asarray(positions, dtype=np.float64)[..., None] * inv_freq(theta, d)
+    table = inv_freq(theta, d) if freqs is None else np.asarray(freqs, np.float64)
+    angle = np.asarray(positions, dtype=np.float64)[..., None] * table
     c, s = np.cos(angle), np.sin(angle)
     x1, x2 = x[..., :half], x[..., half:]
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
 
-def rope_neox_bf16(x_bits, positions, theta):
+def rope_neox_bf16(x_bits, positions, theta, freqs=None):
     """bf16 in -> rotate in float64 -> bf16 out (one rounding)."""
     x = bf16.to_f64(x_bits)                               # [nnz, H, D]
     pos = np.asarray(positions)[:, None]                  # broadcast over heads
-    return bf16.from_f64(rope_neox(x, pos, theta))
+    return bf16.from_f64(rope_neox(x, pos, theta, freqs))
 
 
 def append_status(batch_indices, positions, page_indptr, page_indices, page_refcounts,

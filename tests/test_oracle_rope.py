@@ -4,6 +4,8 @@
   reference for the split-half convention;
 * complex multiplication by exp(i * angle) (numpy complex) for every pair;
 * closed forms of the frequency table; rotation by zero is the identity;
+* the Llama 3.1 table against transformers' own llama3 rope initialisation
+  (float32 there), its three bands against closed forms;
 * group laws: pair norms preserved, R_p R_q = R_{p+q}, scores depend only on
   the position difference;
 * append round trips through the (separately pinned) page-table gather, and
@@ -28,6 +30,54 @@ def test_inv_freq_closed_forms():
     assert f[0] == 1.0
     np.testing.assert_allclose(f[32], 0.01, rtol=1e-15)          # 10000 ** (-1/2)
     np.testing.assert_allclose(f[1:] / f[:-1], 10000.0 ** (-2.0 / D), rtol=1e-14)
+
+
+LLAMA31 = dict(factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0,
+               original_max_position=8192)
+
+
+def test_llama31_table_matches_transformers():
+    from transformers import LlamaConfig
+    from transformers.modeling_rope_utils import ROPE_INIT_FUNCTIONS
+    cfg = LlamaConfig(hidden_size=32 * D, num_attention_heads=32, head_dim=D,
+                      max_position_embeddings=131072,
+                      rope_parameters={"rope_type": "llama3", "rope_theta": 500000.0,
+                                       "factor": 8.0, "low_freq_factor": 1.0,
+                                       "high_freq_factor": 4.0,
+                                       "original_max_position_embeddings": 8192})
+    ref, _ = ROPE_INIT_FUNCTIONS["llama3"](cfg, "cpu")
+    got = R.inv_freq_llama31(500000.0, D, **LLAMA31)
+    np.testing.assert_allclose(got, ref.double().numpy(), rtol=2e-6)
+
+
+def test_llama31_bands():
+    base = R.inv_freq(500000.0, D)
+    got = R.inv_freq_llama31(500000.0, D, **LLAMA31)
+    wl = 2 * np.pi / base
+    hi = wl < 8192 / 4.0
+    lo = wl > 8192 / 1.0
+    assert hi.any() and lo.any() and (~hi & ~lo).any()
+    assert np.array_equal(got[hi], base[hi])          # short wavelengths keep their frequency
+    assert np.array_equal(got[lo], base[lo] / 8.0)    # long ones are slowed by the factor
+    mid = ~hi & ~lo                                   # in between: strictly between the two
+    assert (got[mid] < base[mid]).all() and (got[mid] > base[mid] / 8.0).all()
+    # with factor 1 the table is the standard one
+    same = R.inv_freq_llama31(500000.0, D, 1.0, 1.0, 4.0, 8192)
+    np.testing.assert_allclose(same, base, rtol=1e-15)
+
+
+def test_rope_with_a_table_and_negative_positions():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((20, D))
+    pos = rng.integers(-40000, 40000, size=20)
+    table = R.inv_freq_llama31(500000.0, D, **LLAMA31)
+    z = (x[:, :64] + 1j * x[:, 64:]) * np.exp(1j * pos[:, None] * table)
+    got = R.rope_neox(x, pos, None, freqs=table)
+    np.testing.assert_allclose(got[:, :64], z.real, atol=1e-12)
+    np.testing.assert_allclose(got[:, 64:], z.imag, atol=1e-12)
+    # rotating by p then by -p returns the input
+    back = R.rope_neox(R.rope_neox(x, pos, 10000.0), -pos, 10000.0)
+    np.testing.assert_allclose(back, x, atol=1e-12)
 
 
 def test_matches_transformers_rotate_half():
