@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, TFLOP/s
 ROWS = ("decode", "decode_mha", "decode_mqa", "prefill_ragged", "append", "prefill_paged",
-        "pages_shapes", "merge", "copy")
+        "pages_shapes", "merge", "rope", "copy")
 
 
 def log(msg):
@@ -352,6 +352,33 @@ def bench_merge(torch, oxa, iters=30, warmup=5):
     return res
 
 
+def bench_rope(torch, oxa, iters=20, warmup=3):
+    """Standalone NeoX RoPE of q and k at the long-prefill shape: 32768 tokens,
+    32 q / 8 kv heads, positions 0..16383 twice (out of place)."""
+    nnz, hq, hkv = 32768, 32, 8
+    q = torch.randn(nnz, hq, 128, device="cuda").to(torch.bfloat16)
+    k = torch.randn(nnz, hkv, 128, device="cuda").to(torch.bfloat16)
+    pos = dev(np.tile(np.arange(16384, dtype=np.int32), 2))
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        rc = oxa.oxa_rope_neox(q, qo, k, ko, pos, rope_theta=10000.0)
+        if rc != 0:
+            raise RuntimeError(oxa.status_string(rc))
+
+    for i in range(warmup):
+        call(i)
+    t = LaunchTimer(torch, stream, iters)
+    t.run(call, iters)
+    ms = float(np.mean(t.launch_ms(iters)))
+    nbytes = nnz * (hq + hkv) * 256 * 2 + nnz * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"rope_neox_32768_tok_32q_8kv": {"us": round(ms * 1e3, 1), "GB/s": round(gbs, 1),
+                                            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                                            "bytes": nbytes}}
+
+
 def cpu_baseline(case, budget_s=10.0):
     """The oracle's paged decode of the whole workload, repeated for ~budget_s,
     with its BLAS pool held to one thread."""
@@ -429,6 +456,10 @@ def main():
     if only in (None, "merge"):
         log("merge: attention-state merges (cascade pair, 8 f32 partials)")
         out["merge"] = bench_merge(torch, oxa)
+
+    if only in (None, "rope"):
+        log("rope: standalone NeoX RoPE, 32768 tokens")
+        out["rope"] = bench_rope(torch, oxa)
 
     if only == "copy":
         # a plain device copy of known size: the reference for scaling the HBM
@@ -523,6 +554,8 @@ def main():
         rows["pages_shapes_latency"] = out["pages_shapes"]
     if "merge" in out:
         rows.update(out["merge"])
+    if "rope" in out:
+        rows.update(out["rope"])
     line["rows"] = rows
     if "value" not in line:
         line.update({"value": None, "ms_per_step": None, "config": {"workload": only}})

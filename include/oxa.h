@@ -11,10 +11,11 @@
  *   oxa_ragged_prefill     causal (or full) prefill over packed ragged K/V
  *   oxa_paged_prefill      causal (or full) prefill over paged K/V
  *
- * and a standalone attention-state merge (oxa_merge_states,
- * oxa_merge_state_pair) that combines the (output, lse) states of disjoint
- * key sets, as split-K decode does internally and cascade / shared-prefix
- * attention does across calls.
+ * and two standalone operations: the attention-state merge
+ * (oxa_merge_states, oxa_merge_state_pair), which combines the (output, lse)
+ * states of disjoint key sets as split-K decode does internally and cascade /
+ * shared-prefix attention does across calls, and NeoX RoPE on q and k at
+ * explicit positions (oxa_rope_neox, oxa_rope_llama31).
  *
  * The operator contracts follow the "FlashInfer parity matrix" page (sections
  * "Admitted attention matrix", "Dispatch limits", "Paged KV ownership
@@ -72,7 +73,7 @@
 extern "C" {
 #endif
 
-#define OXA_ABI_VERSION 3
+#define OXA_ABI_VERSION 4
 #define OXA_PAGE_SIZE 16
 #define OXA_HEAD_DIM 128
 
@@ -319,6 +320,50 @@ oxa_status oxa_merge_state_pair(
     const void* v_a, const float* lse_a, const void* v_b, const float* lse_b, int32_t v_dtype,
     int32_t num_rows, int32_t num_heads, int32_t head_dim,
     void* v_out, int32_t out_dtype, float* lse_out);
+
+/*
+ * Standalone NeoX RoPE on q and k at explicit positions.  ("FlashInfer parity
+ * matrix": Admitted attention matrix, row Standard RoPE - head dim 128, NeoX
+ * split-half, explicit int32 positions; Domain coverage, RoPE - the standard
+ * and Llama 3.1 variants.  "Oxide Infer" README, Operator surface: BF16 NeoX
+ * RoPE with explicit positions.)
+ *
+ * For every token t < nnz at position p = positions[t] (any int32; negative
+ * positions rotate backwards) and every head row x of q[t] and k[t]: pair
+ * (x_i, x_{i+64}), i < 64, becomes (x_i cos a - x_{i+64} sin a,
+ * x_{i+64} cos a + x_i sin a) with a = p * f_i, evaluated in double precision
+ * and rounded once to bf16 (nearest even) - the same rotation the fused
+ * oxa_paged_append_rope applies.
+ *
+ * oxa_rope_neox:    f_i = rope_theta^(-2i/128).
+ * oxa_rope_llama31: the Llama 3.1 rescaling of that table.  With wavelength
+ *   w_i = 2 pi / f_i, L = original_max_position: f_i stays if
+ *   w_i < L / high_freq_factor, becomes f_i / factor if w_i > L / low_freq_factor,
+ *   and in between (1 - m) f_i / factor + m f_i with
+ *   m = (L / w_i - low_freq_factor) / (high_freq_factor - low_freq_factor).
+ *   Requires factor > 0, 0 < low_freq_factor < high_freq_factor, L >= 1.
+ *
+ * Shapes: q_in, q_out [nnz][num_qo_heads][128]; k_in, k_out
+ * [nnz][num_kv_heads][128]; positions [nnz].  q_in and q_out are both NULL
+ * (q is skipped; num_qo_heads is ignored) or both set, likewise k_in / k_out;
+ * at least one of the two is set.  q_out may equal q_in and k_out k_in (in
+ * place); any other overlap between the regions is rejected.  nnz == 0 is a
+ * no-op (the tensor pointers may then be NULL).  rope_theta must be finite
+ * and > 0.  No workspace, no status: nothing here depends on the data.
+ */
+oxa_status oxa_rope_neox(
+    hipStream_t stream,
+    const uint16_t* q_in, uint16_t* q_out, int32_t num_qo_heads,
+    const uint16_t* k_in, uint16_t* k_out, int32_t num_kv_heads, int32_t head_dim,
+    const int32_t* positions, int32_t nnz, float rope_theta);
+
+oxa_status oxa_rope_llama31(
+    hipStream_t stream,
+    const uint16_t* q_in, uint16_t* q_out, int32_t num_qo_heads,
+    const uint16_t* k_in, uint16_t* k_out, int32_t num_kv_heads, int32_t head_dim,
+    const int32_t* positions, int32_t nnz, float rope_theta,
+    float factor, float low_freq_factor, float high_freq_factor,
+    int32_t original_max_position);
 
 #ifdef __cplusplus
 }

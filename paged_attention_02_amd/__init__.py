@@ -65,6 +65,8 @@ SIGNATURES = {
     "oxa_paged_prefill_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "oxa_merge_states": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P]),
     "oxa_merge_state_pair": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P]),
+    "oxa_rope_neox": (_I, [_P, _P, _P, _I, _P, _P, _I, _I, _P, _I, _F]),
+    "oxa_rope_llama31": (_I, [_P, _P, _P, _I, _P, _P, _I, _I, _P, _I, _F, _F, _F, _F, _I]),
 }
 
 _lib = None
@@ -276,3 +278,38 @@ def oxa_merge_state_pair(v_a, lse_a, v_b, lse_b, v_out, lse_out=None, *, stream=
         _stream(stream), _ptr(v_a), _f32(lse_a, "lse_a"), _ptr(v_b), _f32(lse_b, "lse_b"),
         _state_dtype(v_a, "v_a"), R, H, D, _ptr(v_out), _state_dtype(v_out, "v_out"),
         _f32(lse_out, "lse_out"))
+
+
+def _rope_args(q_in, q_out, k_in, k_out, positions):
+    ref = q_in if q_in is not None else k_in
+    if ref is None:
+        raise ValueError("pass q_in/q_out, k_in/k_out or both")
+    nnz, _, d = ref.shape
+    hq = q_in.shape[1] if q_in is not None else 0
+    hkv = k_in.shape[1] if k_in is not None else 0
+    if q_in is not None:
+        _shape(q_out, q_in.shape, "q_out")
+    if k_in is not None:
+        _shape(k_in, (nnz, hkv, d), "k_in")
+        _shape(k_out, k_in.shape, "k_out")
+    _shape(positions, (nnz,), "positions")
+    return [_bf16(q_in, "q_in"), _bf16(q_out, "q_out"), hq, _bf16(k_in, "k_in"),
+            _bf16(k_out, "k_out"), hkv, d, _i32(positions, "positions"), nnz]
+
+
+def oxa_rope_neox(q_in, q_out, k_in, k_out, positions, *, rope_theta=10000.0, stream=None) -> int:
+    """NeoX RoPE of q [nnz, Hq, 128] and/or k [nnz, Hkv, 128] at positions [nnz]
+    (int32); pass None for both tensors of a skipped side; outputs may be the
+    inputs themselves."""
+    return lib().oxa_rope_neox(_stream(stream), *_rope_args(q_in, q_out, k_in, k_out, positions),
+                               float(rope_theta))
+
+
+def oxa_rope_llama31(q_in, q_out, k_in, k_out, positions, *, rope_theta=500000.0, factor=8.0,
+                     low_freq_factor=1.0, high_freq_factor=4.0, original_max_position=8192,
+                     stream=None) -> int:
+    """As oxa_rope_neox with the Llama 3.1 frequency table."""
+    return lib().oxa_rope_llama31(_stream(stream),
+                                  *_rope_args(q_in, q_out, k_in, k_out, positions),
+                                  float(rope_theta), float(factor), float(low_freq_factor),
+                                  float(high_freq_factor), int(original_max_position))

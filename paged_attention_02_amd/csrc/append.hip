@@ -145,47 +145,6 @@ __global__ __launch_bounds__(256) void append_check_kernel(AppendParams p) {
   }
 }
 
-// float(x) for the 8 bf16 of a 16-byte chunk
-__device__ __forceinline__ void unpack8(u32x4_t w, float* x) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { x[2 * i] = bf16_lo(w[i]); x[2 * i + 1] = bf16_hi(w[i]); }
-}
-
-// Round-to-nearest-even double -> bf16 for results in bf16's normal range,
-// from the double's bit fields; anything else takes the general routine.
-__device__ __forceinline__ uint32_t bf16_rne(double y) {
-  const uint64_t u = __double_as_longlong(y);
-  const uint32_t hw = (uint32_t)(u >> 32);
-  const uint32_t lw = (uint32_t)u;
-  uint32_t field = (hw >> 13) & 0x3ffffu;            // 11 exponent + 7 fraction bits
-  const uint32_t rb = (hw >> 12) & 1u;
-  const uint32_t sticky = ((hw & 0xfffu) | lw) != 0u;
-  field += rb & (sticky | (field & 1u));
-  const int e = (int)(field >> 7) - 896;
-  if (e >= 1 && e <= 254) return ((hw >> 16) & 0x8000u) | ((uint32_t)e << 7) | (field & 0x7fu);
-  return bf16_from_double_rne(y);
-}
-
-// Rotate one 8-pair chunk: x1 = dims [8f, 8f+8), x2 = dims [64+8f, 64+8f+8).
-__device__ __forceinline__ void rotate_chunk(u32x4_t w1, u32x4_t w2, const double* c,
-                                             const double* s, u32x4_t* out1, u32x4_t* out2) {
-  float x1[8], x2[8];
-  unpack8(w1, x1);
-  unpack8(w2, x2);
-  uint32_t y1[8], y2[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const double a = x1[i], bb = x2[i];
-    y1[i] = bf16_rne(a * c[i] - bb * s[i]);
-    y2[i] = bf16_rne(bb * c[i] + a * s[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    (*out1)[i] = y1[2 * i] | (y1[2 * i + 1] << 16);
-    (*out2)[i] = y2[2 * i] | (y2[2 * i + 1] << 16);
-  }
-}
-
 // Grid-stride over tokens, one wave per token at a time.  Lane l evaluates
 // the sin/cos of frequency l and shares it through a wave-private LDS slot;
 // lane l then rotates the frequency chunk f = l % 8 (frequencies 8f .. 8f+7)

@@ -83,4 +83,17 @@ hipError_t launch_merge_states(const MergeLaunch& a, hipStream_t stream);
 // Work-groups launch_merge_states uses for `units` units.
 int64_t merge_states_groups(int64_t units, int in_f32);
 
+// Standalone NeoX RoPE: q (if q_in) and k (if k_in) of nnz tokens rotated at
+// positions[t] with the given double-precision frequency table.
+struct RopeLaunch {
+  const uint16_t* q_in;
+  uint16_t* q_out;
+  const uint16_t* k_in;
+  uint16_t* k_out;
+  const int32_t* positions;
+  int32_t hq, hkv, nnz;
+  double inv_freq[64];
+};
+hipError_t launch_rope(const RopeLaunch& a, hipStream_t stream);
+
 }  // namespace oxa

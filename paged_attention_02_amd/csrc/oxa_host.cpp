@@ -78,6 +78,24 @@ oxa_status check_merge_shape(int32_t num_rows, int32_t num_states, int32_t num_h
   return OXA_OK;
 }
 
+// The Llama 3.1 frequency table, evaluated step by step in double precision
+// without fused multiply-adds.
+void llama31_table(double theta, double factor, double low, double high, int32_t orig,
+                   double* out) {
+#pragma clang fp contract(off)
+  const double low_wl = (double)orig / low;
+  const double high_wl = (double)orig / high;
+  for (int i = 0; i < 64; ++i) {
+    const double base = std::pow(theta, -2.0 * (double)i / (double)OXA_HEAD_DIM);
+    const double wl = 2.0 * M_PI / base;
+    const double smooth = ((double)orig / wl - low) / (high - low);
+    const double blended = (1.0 - smooth) * base / factor + smooth * base;
+    double f = wl > low_wl ? base / factor : blended;
+    if (wl < high_wl) f = base;
+    out[i] = f;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -493,6 +511,81 @@ oxa_status oxa_merge_state_pair(hipStream_t stream, const void* v_a, const float
   m.out = v_out;
   m.lse_out = lse_out;
   return launch_status(oxa::launch_merge_states(m, stream));
+}
+
+// ---------------------------------------------------------------- RoPE
+
+namespace {
+
+// Checks shared by both RoPE entry points; fills everything but the table.
+oxa_status rope_setup(const uint16_t* q_in, uint16_t* q_out, int32_t num_qo_heads,
+                      const uint16_t* k_in, uint16_t* k_out, int32_t num_kv_heads,
+                      int32_t head_dim, const int32_t* positions, int32_t nnz, float rope_theta,
+                      oxa::RopeLaunch* a) {
+  if ((q_in == nullptr) != (q_out == nullptr) || (k_in == nullptr) != (k_out == nullptr))
+    return OXA_ERR_NULL;
+  const bool has_q = q_in != nullptr, has_k = k_in != nullptr;
+  if (nnz != 0 && ((!has_q && !has_k) || positions == nullptr)) return OXA_ERR_NULL;
+  if (head_dim != OXA_HEAD_DIM) return OXA_ERR_UNSUPPORTED;
+  if (nnz < 0 || (has_q && num_qo_heads < 1) || (has_k && num_kv_heads < 1)) return OXA_ERR_SHAPE;
+  if (!(rope_theta > 0.f) || !std::isfinite(rope_theta)) return OXA_ERR_SHAPE;
+  if (!aligned(q_in, 16) || !aligned(q_out, 16) || !aligned(k_in, 16) || !aligned(k_out, 16) ||
+      !aligned(positions, 4))
+    return OXA_ERR_ALIGN;
+  const uint64_t n = (uint64_t)nnz;
+  const uint64_t qb = has_q ? n * (uint64_t)num_qo_heads * kRowBytes : 0;
+  const uint64_t kb = has_k ? n * (uint64_t)num_kv_heads * kRowBytes : 0;
+  const Region qi{q_in, qb}, ki{k_in, kb}, pi{positions, n * 4};
+  const Region qo{q_out == q_in ? nullptr : q_out, qb}, ko{k_out == k_in ? nullptr : k_out, kb};
+  // outputs written in place count as their input region
+  const Region qw{q_out, qb}, kw{k_out, kb};
+  if (overlaps(qw, kw) || overlaps(qw, ki) || overlaps(qw, pi) || overlaps(kw, qi) ||
+      overlaps(kw, pi) || overlaps(qo, qi) || overlaps(ko, ki))
+    return OXA_ERR_ALIAS;
+  a->q_in = q_in;
+  a->q_out = q_out;
+  a->k_in = k_in;
+  a->k_out = k_out;
+  a->positions = positions;
+  a->hq = has_q ? num_qo_heads : 0;
+  a->hkv = has_k ? num_kv_heads : 0;
+  a->nnz = nnz;
+  return OXA_OK;
+}
+
+}  // namespace
+
+oxa_status oxa_rope_neox(hipStream_t stream, const uint16_t* q_in, uint16_t* q_out,
+                         int32_t num_qo_heads, const uint16_t* k_in, uint16_t* k_out,
+                         int32_t num_kv_heads, int32_t head_dim, const int32_t* positions,
+                         int32_t nnz, float rope_theta) {
+  oxa::RopeLaunch a;
+  if (oxa_status s = rope_setup(q_in, q_out, num_qo_heads, k_in, k_out, num_kv_heads, head_dim,
+                                positions, nnz, rope_theta, &a))
+    return s;
+  if (nnz == 0) return OXA_OK;
+  for (int i = 0; i < 64; ++i)
+    a.inv_freq[i] = std::pow((double)rope_theta, -2.0 * (double)i / (double)OXA_HEAD_DIM);
+  return launch_status(oxa::launch_rope(a, stream));
+}
+
+oxa_status oxa_rope_llama31(hipStream_t stream, const uint16_t* q_in, uint16_t* q_out,
+                            int32_t num_qo_heads, const uint16_t* k_in, uint16_t* k_out,
+                            int32_t num_kv_heads, int32_t head_dim, const int32_t* positions,
+                            int32_t nnz, float rope_theta, float factor, float low_freq_factor,
+                            float high_freq_factor, int32_t original_max_position) {
+  oxa::RopeLaunch a;
+  if (oxa_status s = rope_setup(q_in, q_out, num_qo_heads, k_in, k_out, num_kv_heads, head_dim,
+                                positions, nnz, rope_theta, &a))
+    return s;
+  if (!(factor > 0.f) || !std::isfinite(factor) || !(low_freq_factor > 0.f) ||
+      !(high_freq_factor > low_freq_factor) || !std::isfinite(high_freq_factor) ||
+      original_max_position < 1)
+    return OXA_ERR_SHAPE;
+  if (nnz == 0) return OXA_OK;
+  llama31_table((double)rope_theta, factor, low_freq_factor, high_freq_factor,
+                original_max_position, a.inv_freq);
+  return launch_status(oxa::launch_rope(a, stream));
 }
 
 }  // extern "C"

@@ -20,7 +20,8 @@ def test_every_declared_symbol_is_exported():
     lib = ensure_built()
     names = declared_functions()
     assert {"oxa_paged_append_rope", "oxa_paged_decode", "oxa_ragged_prefill",
-            "oxa_paged_prefill", "oxa_merge_states", "oxa_merge_state_pair"} <= set(names)
+            "oxa_paged_prefill", "oxa_merge_states", "oxa_merge_state_pair", "oxa_rope_neox",
+            "oxa_rope_llama31"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
         assert n in oxa.SIGNATURES, f"binding lacks a signature for {n}"
@@ -28,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     lib = ensure_built()
-    assert lib.oxa_abi_version() == 3
+    assert lib.oxa_abi_version() == 4
     assert oxa.status_string(0) == "OXA_OK"
     assert oxa.status_string(20) == "OXA_DEV_NOT_EXCLUSIVE"
     assert oxa.status_string(999) == "unknown"

@@ -263,3 +263,30 @@ def test_merge_graph_replays_equal_eager():
         torch.cuda.synchronize()
         for a, b in zip(outs["g"], outs["e"]):
             assert torch.equal(a, b), f"replay {rep} differs from eager"
+
+
+def test_rope_graph_replays_equal_eager():
+    rng = np.random.default_rng(3100)
+    nnz, hq, hkv = 4096, 32, 8
+    q = dev(W.bf16_normal(rng, (nnz, hq, 128)))
+    k = dev(W.bf16_normal(rng, (nnz, hkv, 128)))
+    pos = dev(rng.integers(0, 32768, nnz).astype(np.int32))
+    outs = {w: (torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)) for w in ("g", "e")}
+    ensure_built()
+
+    def call(which):
+        qo, ko, ko2 = outs[which]
+        ok(oxa.oxa_rope_neox(q, qo, k, ko, pos))
+        ok(oxa.oxa_rope_llama31(None, None, k, ko2, pos))
+
+    note("graph rope: capture")
+    g = capture(lambda: call("g"))
+    for rep in range(REPLAYS):
+        pos.copy_(dev(rng.integers(-70000, 70000, nnz).astype(np.int32)))
+        k.copy_(dev(W.bf16_normal(rng, (nnz, hkv, 128))))
+        note(f"graph rope: replay {rep}")
+        g.replay()
+        call("e")
+        torch.cuda.synchronize()
+        for a, b in zip(outs["g"], outs["e"]):
+            assert torch.equal(a, b), f"replay {rep} differs from eager"

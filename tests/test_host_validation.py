@@ -202,3 +202,54 @@ def call_pair(**over):
 ])
 def test_merge_state_pair_rejections(over, code):
     assert call_pair(**over) == code
+
+
+def call_rope(llama=False, **over):
+    args = dict(stream=None, q_in=addr(0), q_out=addr(1), hq=8, k_in=addr(2), k_out=addr(3),
+                hkv=2, head_dim=128, pos=addr(4), nnz=10, theta=10000.0)
+    extra = dict(factor=8.0, low=1.0, high=4.0, orig=8192)
+    args.update({k: v for k, v in over.items() if k in args})
+    extra.update({k: v for k, v in over.items() if k in extra})
+    lib = ensure_built()
+    if llama:
+        return lib.oxa_rope_llama31(*args.values(), *extra.values())
+    return lib.oxa_rope_neox(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q_out=None), oxa.OXA_ERR_NULL),                 # q_in without q_out
+    (dict(k_in=None), oxa.OXA_ERR_NULL),                  # k_out without k_in
+    (dict(pos=None), oxa.OXA_ERR_NULL),
+    (dict(q_in=None, q_out=None, k_in=None, k_out=None), oxa.OXA_ERR_NULL),
+    (dict(head_dim=64), oxa.OXA_ERR_UNSUPPORTED),
+    (dict(nnz=-1), oxa.OXA_ERR_SHAPE),
+    (dict(hq=0), oxa.OXA_ERR_SHAPE),
+    (dict(theta=-1.0), oxa.OXA_ERR_SHAPE),
+    (dict(theta=float("nan")), oxa.OXA_ERR_SHAPE),
+    (dict(k_out=addr(3) + 8), oxa.OXA_ERR_ALIGN),
+    (dict(pos=addr(4) + 2), oxa.OXA_ERR_ALIGN),
+    (dict(q_out=addr(0) + 256), oxa.OXA_ERR_ALIAS),       # shifted onto q_in
+    (dict(k_out=addr(1)), oxa.OXA_ERR_ALIAS),             # k_out over q_out
+    (dict(q_out=addr(2)), oxa.OXA_ERR_ALIAS),             # q_out over k_in
+    (dict(pos=addr(3) + 64), oxa.OXA_ERR_ALIAS),          # positions inside k_out
+])
+def test_rope_rejections(over, code):
+    assert call_rope(**over) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(factor=0.0), oxa.OXA_ERR_SHAPE),
+    (dict(low=0.0), oxa.OXA_ERR_SHAPE),
+    (dict(high=1.0), oxa.OXA_ERR_SHAPE),                 # high must exceed low
+    (dict(orig=0), oxa.OXA_ERR_SHAPE),
+    (dict(factor=float("inf")), oxa.OXA_ERR_SHAPE),
+    (dict(theta=0.0), oxa.OXA_ERR_SHAPE),
+    (dict(pos=None), oxa.OXA_ERR_NULL),
+])
+def test_rope_llama31_rejections(over, code):
+    assert call_rope(llama=True, **over) == code
+
+
+def test_rope_with_no_tokens_is_a_no_op():
+    assert call_rope(nnz=0, q_in=None, q_out=None, k_in=None, k_out=None, pos=None) == oxa.OXA_OK
+    assert call_rope(llama=True, nnz=0, pos=None) == oxa.OXA_OK
