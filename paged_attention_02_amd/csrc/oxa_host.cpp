@@ -96,6 +96,54 @@ void llama31_table(double theta, double factor, double low, double high, int32_t
   }
 }
 
+
+// Query tiles per sequence for the given head grouping (256 columns per
+// work-group, BM = 256 / min(group, 256) rows each).  The prefill schedule
+// orders at most kMaxPrefillTiles tile indices.
+uint64_t prefill_tiles(int32_t hq, int32_t hkv, int32_t max_qo_len) {
+  const int32_t group = hq / hkv;
+  const int32_t gwg = group < 256 ? group : 256;
+  const int32_t bm = 256 / gwg;
+  return ((uint64_t)max_qo_len + bm - 1) / bm;
+}
+
+
+// Checks shared by both RoPE entry points; fills everything but the table.
+oxa_status rope_setup(const uint16_t* q_in, uint16_t* q_out, int32_t num_qo_heads,
+                      const uint16_t* k_in, uint16_t* k_out, int32_t num_kv_heads,
+                      int32_t head_dim, const int32_t* positions, int32_t nnz, float rope_theta,
+                      oxa::RopeLaunch* a) {
+  if ((q_in == nullptr) != (q_out == nullptr) || (k_in == nullptr) != (k_out == nullptr))
+    return OXA_ERR_NULL;
+  const bool has_q = q_in != nullptr, has_k = k_in != nullptr;
+  if (nnz != 0 && ((!has_q && !has_k) || positions == nullptr)) return OXA_ERR_NULL;
+  if (head_dim != OXA_HEAD_DIM) return OXA_ERR_UNSUPPORTED;
+  if (nnz < 0 || (has_q && num_qo_heads < 1) || (has_k && num_kv_heads < 1)) return OXA_ERR_SHAPE;
+  if (!(rope_theta > 0.f) || !std::isfinite(rope_theta)) return OXA_ERR_SHAPE;
+  if (!aligned(q_in, 16) || !aligned(q_out, 16) || !aligned(k_in, 16) || !aligned(k_out, 16) ||
+      !aligned(positions, 4))
+    return OXA_ERR_ALIGN;
+  const uint64_t n = (uint64_t)nnz;
+  const uint64_t qb = has_q ? n * (uint64_t)num_qo_heads * kRowBytes : 0;
+  const uint64_t kb = has_k ? n * (uint64_t)num_kv_heads * kRowBytes : 0;
+  const Region qi{q_in, qb}, ki{k_in, kb}, pi{positions, n * 4};
+  const Region qo{q_out == q_in ? nullptr : q_out, qb}, ko{k_out == k_in ? nullptr : k_out, kb};
+  // outputs written in place count as their input region
+  const Region qw{q_out, qb}, kw{k_out, kb};
+  if (overlaps(qw, kw) || overlaps(qw, ki) || overlaps(qw, pi) || overlaps(kw, qi) ||
+      overlaps(kw, pi) || overlaps(qo, qi) || overlaps(ko, ki))
+    return OXA_ERR_ALIAS;
+  a->q_in = q_in;
+  a->q_out = q_out;
+  a->k_in = k_in;
+  a->k_out = k_out;
+  a->positions = positions;
+  a->hq = has_q ? num_qo_heads : 0;
+  a->hkv = has_k ? num_kv_heads : 0;
+  a->nnz = nnz;
+  return OXA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -291,19 +339,6 @@ oxa_status oxa_paged_decode(hipStream_t stream, const uint16_t* q, int32_t batch
 size_t oxa_ragged_prefill_workspace_bytes(int32_t, int32_t, int32_t, int32_t) { return 0; }
 size_t oxa_paged_prefill_workspace_bytes(int32_t, int32_t, int32_t, int32_t) { return 0; }
 
-namespace {
-
-// Query tiles per sequence for the given head grouping (256 columns per
-// work-group, BM = 256 / min(group, 256) rows each).  The prefill schedule
-// orders at most kMaxPrefillTiles tile indices.
-uint64_t prefill_tiles(int32_t hq, int32_t hkv, int32_t max_qo_len) {
-  const int32_t group = hq / hkv;
-  const int32_t gwg = group < 256 ? group : 256;
-  const int32_t bm = 256 / gwg;
-  return ((uint64_t)max_qo_len + bm - 1) / bm;
-}
-
-}  // namespace
 
 oxa_status oxa_ragged_prefill(hipStream_t stream, const uint16_t* q, const uint16_t* k,
                               const uint16_t* v, const int32_t* qo_indptr,
@@ -515,45 +550,6 @@ oxa_status oxa_merge_state_pair(hipStream_t stream, const void* v_a, const float
 
 // ---------------------------------------------------------------- RoPE
 
-namespace {
-
-// Checks shared by both RoPE entry points; fills everything but the table.
-oxa_status rope_setup(const uint16_t* q_in, uint16_t* q_out, int32_t num_qo_heads,
-                      const uint16_t* k_in, uint16_t* k_out, int32_t num_kv_heads,
-                      int32_t head_dim, const int32_t* positions, int32_t nnz, float rope_theta,
-                      oxa::RopeLaunch* a) {
-  if ((q_in == nullptr) != (q_out == nullptr) || (k_in == nullptr) != (k_out == nullptr))
-    return OXA_ERR_NULL;
-  const bool has_q = q_in != nullptr, has_k = k_in != nullptr;
-  if (nnz != 0 && ((!has_q && !has_k) || positions == nullptr)) return OXA_ERR_NULL;
-  if (head_dim != OXA_HEAD_DIM) return OXA_ERR_UNSUPPORTED;
-  if (nnz < 0 || (has_q && num_qo_heads < 1) || (has_k && num_kv_heads < 1)) return OXA_ERR_SHAPE;
-  if (!(rope_theta > 0.f) || !std::isfinite(rope_theta)) return OXA_ERR_SHAPE;
-  if (!aligned(q_in, 16) || !aligned(q_out, 16) || !aligned(k_in, 16) || !aligned(k_out, 16) ||
-      !aligned(positions, 4))
-    return OXA_ERR_ALIGN;
-  const uint64_t n = (uint64_t)nnz;
-  const uint64_t qb = has_q ? n * (uint64_t)num_qo_heads * kRowBytes : 0;
-  const uint64_t kb = has_k ? n * (uint64_t)num_kv_heads * kRowBytes : 0;
-  const Region qi{q_in, qb}, ki{k_in, kb}, pi{positions, n * 4};
-  const Region qo{q_out == q_in ? nullptr : q_out, qb}, ko{k_out == k_in ? nullptr : k_out, kb};
-  // outputs written in place count as their input region
-  const Region qw{q_out, qb}, kw{k_out, kb};
-  if (overlaps(qw, kw) || overlaps(qw, ki) || overlaps(qw, pi) || overlaps(kw, qi) ||
-      overlaps(kw, pi) || overlaps(qo, qi) || overlaps(ko, ki))
-    return OXA_ERR_ALIAS;
-  a->q_in = q_in;
-  a->q_out = q_out;
-  a->k_in = k_in;
-  a->k_out = k_out;
-  a->positions = positions;
-  a->hq = has_q ? num_qo_heads : 0;
-  a->hkv = has_k ? num_kv_heads : 0;
-  a->nnz = nnz;
-  return OXA_OK;
-}
-
-}  // namespace
 
 oxa_status oxa_rope_neox(hipStream_t stream, const uint16_t* q_in, uint16_t* q_out,
                          int32_t num_qo_heads, const uint16_t* k_in, uint16_t* k_out,
