@@ -17,8 +17,9 @@
 // the causal diagonal or the sequence end, updates the f32 online softmax
 // (lazy rescaling), and accumulates O^T = V^T * P^T (32 more MFMAs; V^T
 // through the LDS transpose read, P^T straight from the score registers).
-// K/V tiles are double-buffered: the next tile's loads are in flight during
-// the current tile's math.  Tiles are scheduled longest-first: the
+// K/V tiles are double-buffered in LDS: the next tile streams from memory
+// straight into the other buffer (no register staging) during the current
+// tile's math.  Tiles are scheduled longest-first: the
 // query-tile index is the slowest grid dimension, counted from the end.
 #include <atomic>
 
@@ -106,46 +107,55 @@ __device__ __forceinline__ SeqInfo seq_info(const PrefillParams& p, int b) {
 
 constexpr int kPidWin = 2048;  // page ids staged in LDS per window (paged K/V)
 
-// Issue the loads of K/V tile `kt` (64 keys): thread tid brings the 16-byte
-// chunk `tid % 16` of rows tid/16 + (kNW * 4) * u, so 16 lanes read one whole
-// 256-byte row.  Loads are unconditional - straight-line code keeps the wait
-// counters exact - and rows that do not exist read a valid stand-in (key 0 of
-// the sequence, or page 0); `ok` marks the real rows for store_tile.
-template <bool PAGED, int LAYOUT>
-__device__ __forceinline__ void load_tile(const PrefillParams& p, const SeqInfo& si, int kvh,
-                                          int kt, int tid, const int* pids, int wbase,
-                                          u32x4_t* kr, u32x4_t* vr, bool* ok) {
-#pragma unroll
-  for (int u = 0; u < kLoadIters; ++u) {
-    const int row = (tid >> 4) + kNW * 4 * u;
-    const int piece = tid & 15;
-    const int key = kt * kBN + row;
-    int64_t off;
-    if (!PAGED) {
-      ok[u] = key < si.klen;
-      const int kc = ok[u] ? key : 0;
-      off = ((int64_t)(si.kbase + kc) * p.hkv + kvh) * kHeadDim;
-    } else {
-      const int pid = key < si.klen ? pids[key / kPage - wbase] : -1;
-      ok[u] = pid >= 0;
-      const int pc = ok[u] ? pid : 0;
-      const int slot = key & (kPage - 1);
-      off = LAYOUT == 0 ? (((int64_t)pc * kPage + slot) * p.hkv + kvh) * kHeadDim
-                        : (((int64_t)pc * p.hkv + kvh) * kPage + slot) * kHeadDim;
-    }
-    kr[u] = ldg16(p.k + off + piece * 8);
-    vr[u] = ldg16(p.v + off + piece * 8);
-  }
+// LDS byte address of a pointer into shared memory (wave-uniform here).
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)(p));
 }
 
-__device__ __forceinline__ void store_tile(unsigned char* ks, unsigned char* vs, int tid,
-                                           const u32x4_t* kr, const u32x4_t* vr, const bool* ok) {
+// 16 bytes per lane from global memory straight into LDS at base + 16 * lane
+// (global_load_lds_dwordx4, LDS base in M0).  Written as an instruction the
+// compiler does not track: a tracked one makes it wait for the transfer before
+// the next read of any LDS, which would serialise the load of tile kt+1 with
+// the math on tile kt.  The kernel waits for its transfers itself (vmcnt)
+// before the barrier that hands a buffer to its readers.
+__device__ __forceinline__ void dma16(const uint16_t* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(lds_base) : "memory", "m0");
+}
+
+// Bring K/V tile `kt` (64 keys) straight into LDS: wave w fills rows
+// 8w .. 8w+7 with two 16-byte-per-lane loads for K and two for V, each lane
+// writing one fixed 16-byte slot of a 4-row block.  The lane at slot `pos` of
+// row r fetches the chunk that the XOR swizzle places there (chunk pos ^ sw(r)),
+// so the tile lands in the swizzled layout the readers expect.  Keys past the
+// sequence end re-read its last key (finite data; their scores are masked), and
+// a key on an invalid page reads page 0 (the sequence's status is then non-zero
+// and its rows are unspecified), so every load stays inside K and V.
+template <bool PAGED, int LAYOUT>
+__device__ __forceinline__ void issue_tile(const PrefillParams& p, const SeqInfo& si, int kvh,
+                                           int kt, int wave, int lane, const int* pids,
+                                           int wbase, unsigned char* ks, unsigned char* vs) {
 #pragma unroll
   for (int u = 0; u < kLoadIters; ++u) {
-    const int off = swz_off((tid >> 4) + kNW * 4 * u, tid & 15);
-    const u32x4_t z = u32x4_t{0, 0, 0, 0};
-    *reinterpret_cast<u32x4_t*>(ks + off) = ok[u] ? kr[u] : z;
-    *reinterpret_cast<u32x4_t*>(vs + off) = ok[u] ? vr[u] : z;
+    const int row = wave * (4 * kLoadIters) + 4 * u + (lane >> 4);
+    const int pos = lane & 15;
+    const int sw = ((row & 3) << 2) | ((row >> 2) & 3);
+    const int chunk = pos ^ sw;
+    const int key = min(kt * kBN + row, si.klen - 1);
+    int64_t off;
+    if (!PAGED) {
+      off = ((int64_t)(si.kbase + key) * p.hkv + kvh) * kHeadDim;
+    } else {
+      const int pid = max(pids[key / kPage - wbase], 0);
+      const int slot = key & (kPage - 1);
+      off = LAYOUT == 0 ? (((int64_t)pid * kPage + slot) * p.hkv + kvh) * kHeadDim
+                        : (((int64_t)pid * p.hkv + kvh) * kPage + slot) * kHeadDim;
+    }
+    off += chunk * 8;
+    const int lds_off = (wave * (4 * kLoadIters) + 4 * u) * 256;
+    dma16(p.k + off, lds_addr(ks + lds_off));
+    dma16(p.v + off, lds_addr(vs + lds_off));
   }
 }
 
@@ -360,12 +370,9 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
   if (PAGED) stage_pids(0);
   __syncthreads();
 
-  u32x4_t kr[kLoadIters], vr[kLoadIters];
-  bool okr[kLoadIters];
-  if (ntiles > 0) {
-    load_tile<PAGED, LAYOUT>(p, si, kvh, 0, tid, pids, wbase, kr, vr, okr);
-    store_tile(smem, smem + kTileBytes, tid, kr, vr, okr);
-  }
+  if (ntiles > 0)
+    issue_tile<PAGED, LAYOUT>(p, si, kvh, 0, wave, lane, pids, wbase, smem, smem + kTileBytes);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int kt = 0; kt < ntiles; ++kt) {
@@ -379,7 +386,10 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
       stage_pids(wbase);
       __syncthreads();
     }
-    if (kt + 1 < ntiles) load_tile<PAGED, LAYOUT>(p, si, kvh, kt + 1, tid, pids, wbase, kr, vr, okr);
+    if (kt + 1 < ntiles) {  // tile kt+1 streams into the other buffer meanwhile
+      unsigned char* kn = smem + ((kt + 1) & 1) * 2 * kTileBytes;
+      issue_tile<PAGED, LAYOUT>(p, si, kvh, kt + 1, wave, lane, pids, wbase, kn, kn + kTileBytes);
+    }
 
     const int key0 = kt * kBN;
     const bool need_mask = (key0 + kBN > si.klen) || (p.causal && key0 + kBN - 1 > wg_min_lim);
@@ -461,10 +471,7 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
       }
     }
 
-    if (kt + 1 < ntiles) {
-      unsigned char* kn = smem + ((kt + 1) & 1) * 2 * kTileBytes;
-      store_tile(kn, kn + kTileBytes, tid, kr, vr, okr);
-    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile kt+1 has landed in LDS
     __syncthreads();
   }
 
