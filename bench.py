@@ -504,7 +504,7 @@ def main():
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": traffic,
                          "kernel": "paged_decode_kernel" + ("" if r["partitions"] == 1 else
-                                                            " + merge_partials_kernel"),
+                                                            " + merge_states_kernel"),
                          "launch_us_mean": round(lm * 1e3, 2),
                          "launch_us_p10_p50_p90": [round(float(x) * 1e3, 2) for x in
                                                    np.percentile(r["launch_ms"], [10, 50, 90])]},

@@ -31,7 +31,8 @@
  * Memory.  Every tensor pointer is a DEVICE pointer (hipMalloc'd or a torch
  *          CUDA tensor), except where a comment says "host".  The caller owns
  *          all memory.  The library allocates nothing, frees nothing, keeps no
- *          pointer after the call returns and has no global mutable state.
+ *          pointer after the call returns and keeps no state between calls
+ *          apart from a per-device cache of the compute-unit count.
  * Stream.  Work is enqueued on `stream` (0 = the null stream) and the call
  *          returns without synchronising.  Buffers must stay valid, and inputs
  *          unmodified, until that work completes.
