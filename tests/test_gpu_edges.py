@@ -1,0 +1,138 @@
+"""Edge cases and maximum sizes on the GPU.
+
+* ragged causal prefill with empty sequences (no query rows, and no keys)
+  between real ones, against the oracle;
+* extreme head groupings in prefill: 64, 256 and 512 q heads on one kv head
+  (a work-group's 256 columns then hold 4 query rows, 1 row, and one row of
+  half of the heads);
+* 1100 sequences of one query row each: the prefill schedule selects the
+  sequence of an item in several 512-sequence chunks of the batch;
+* paged decode with the largest number of explicit partitions (1024), most
+  of them empty;
+* paged decode at the largest batch (65535 sequences of one token): each
+  output equals the V row of its only key exactly (in value: -0 comes out
+  as +0, since the accumulator starts at +0).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import attention as A
+from oracle import bf16
+from tests.gpu_helpers import assert_attention_close, assert_lse_close, dev, host, host_bits, note
+from tests.lib_loader import ensure_built
+
+import paged_attention_02_amd as oxa
+
+pytestmark = pytest.mark.gpu
+
+
+def ragged(case, causal=True):
+    ensure_built()
+    q = dev(case.q)
+    o = torch.zeros_like(q)
+    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device="cuda")
+    B = len(case.qo_indptr) - 1
+    status = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    rc = oxa.oxa_ragged_prefill(q, dev(case.k), dev(case.v), dev(case.qo_indptr),
+                                dev(case.kv_indptr), o,
+                                max_qo_len=max(1, int(np.diff(case.qo_indptr).max())),
+                                max_kv_len=max(1, int(np.diff(case.kv_indptr).max())),
+                                sm_scale=case.sm_scale, causal=causal, lse=lse, status=status)
+    assert rc == oxa.OXA_OK, oxa.status_string(rc)
+    torch.cuda.synchronize()
+    return host_bits(o), host(lse), host(status)
+
+
+def test_ragged_prefill_with_empty_sequences():
+    qo = [0, 5, 0, 70, 0, 1]
+    kv = [0, 5, 3, 100, 9, 1]
+    case = W.ragged_case(4100, qo_lens=qo, kv_lens=kv, num_qo_heads=8, num_kv_heads=2)
+    note("ragged prefill with empty sequences")
+    o, lse, status = ragged(case)
+    assert (status == 0).all()
+    o_ref, lse_ref = A.ragged_prefill(case.q, case.k, case.v, case.qo_indptr, case.kv_indptr,
+                                      case.sm_scale, True)
+    assert_attention_close(o, o_ref, "empty sequences")
+    assert_lse_close(lse, lse_ref)
+
+
+@pytest.mark.parametrize("hq", [64, 256, 512])
+def test_prefill_extreme_head_groupings(hq):
+    case = W.ragged_case(4200 + hq, qo_lens=[3, 9, 20], kv_lens=[10, 9, 60], num_qo_heads=hq,
+                         num_kv_heads=1)
+    note(f"ragged prefill {hq} q heads on one kv head")
+    o, lse, status = ragged(case)
+    assert (status == 0).all()
+    o_ref, lse_ref = A.ragged_prefill(case.q, case.k, case.v, case.qo_indptr, case.kv_indptr,
+                                      case.sm_scale, True)
+    assert_attention_close(o, o_ref, f"hq={hq}")
+    assert_lse_close(lse, lse_ref)
+
+
+def test_prefill_1100_one_row_sequences():
+    rng = np.random.default_rng(4300)
+    kv = [int(x) for x in rng.integers(1, 64, size=1100)]
+    case = W.ragged_case(4300, qo_lens=[1] * 1100, kv_lens=kv, num_qo_heads=8, num_kv_heads=2)
+    note("ragged prefill 1100 one-row sequences")
+    o, lse, status = ragged(case)
+    assert (status == 0).all()
+    o_ref, lse_ref = A.ragged_prefill(case.q, case.k, case.v, case.qo_indptr, case.kv_indptr,
+                                      case.sm_scale, True)
+    assert_attention_close(o, o_ref, "1100 sequences")
+    assert_lse_close(lse, lse_ref)
+
+
+def test_decode_with_1024_partitions():
+    lens = [1, 33, 700, 5000]
+    case = W.decode_case(4400, batch=4, num_qo_heads=8, num_kv_heads=2, seq_lens=lens,
+                         num_partitions=1024, poison=True)
+    ensure_built()
+    kv = case.kv
+    q = dev(case.q)
+    o = torch.empty_like(q)
+    lse = torch.empty(4, 8, dtype=torch.float32, device="cuda")
+    nbytes = oxa.oxa_paged_decode_workspace_bytes(4, 8, 1024)
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    note("decode with 1024 partitions")
+    rc = oxa.oxa_paged_decode(q, dev(kv.k_pool), dev(kv.v_pool), dev(kv.page_indptr),
+                              dev(kv.page_indices), dev(kv.seq_lens), o,
+                              max_seq_len=case.max_seq_len, sm_scale=case.sm_scale,
+                              num_kv_heads=2, num_partitions=1024, workspace=ws, lse=lse)
+    assert rc == oxa.OXA_OK
+    torch.cuda.synchronize()
+    o_ref, lse_ref = A.paged_decode(case.q, kv.k_pool, kv.v_pool, "NHD", kv.page_indptr,
+                                    kv.page_indices, kv.seq_lens, case.sm_scale)
+    assert_attention_close(host_bits(o), o_ref, "1024 partitions")
+    assert_lse_close(host(lse), lse_ref)
+
+
+def test_decode_at_the_largest_batch():
+    # 65535 sequences of one token each, 2 q heads on 1 kv head; sequence b
+    # owns page perm[b], whose slot 0 holds its only key
+    B = 65535
+    rng = np.random.default_rng(4500)
+    perm = rng.permutation(B).astype(np.int32)
+    k_pool = np.zeros((B, 16, 1, 128), np.uint16)
+    v_pool = np.full((B, 16, 1, 128), W.NAN_BITS, np.uint16)     # unused slots poisoned
+    k_pool[:, 0] = W.bf16_normal(rng, (B, 1, 128))
+    v_pool[:, 0] = W.bf16_normal(rng, (B, 1, 128))
+    q = W.bf16_normal(rng, (B, 2, 128))
+    ensure_built()
+    qd = dev(q)
+    o = torch.empty_like(qd)
+    status = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    note("decode at batch 65535")
+    rc = oxa.oxa_paged_decode(qd, dev(k_pool), dev(v_pool),
+                              dev(np.arange(B + 1, dtype=np.int32)), dev(perm),
+                              dev(np.ones(B, np.int32)), o, max_seq_len=1, sm_scale=0.088,
+                              num_kv_heads=1, status=status)
+    assert rc == oxa.OXA_OK
+    torch.cuda.synchronize()
+    assert (host(status) == 0).all()
+    # the value of the only key's V row, exactly; the accumulator starts at +0,
+    # so a -0 element of V comes out as +0 (equal in value)
+    got = bf16.to_f64(host_bits(o))
+    want = bf16.to_f64(v_pool[perm, 0])                         # [B, 1, 128]
+    assert np.array_equal(got[:, 0], want[:, 0]) and np.array_equal(got[:, 1], want[:, 0])

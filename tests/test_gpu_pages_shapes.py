@@ -1,7 +1,7 @@
 """Attention shapes printed in the Oxide Infer README, Performance snapshot,
 on the GPU vs the FP64 oracle.
 
-Paged decode B1 / KV1 (MHA), ragged causal prefill MHA Q16 / KV16, and ragged
+Paged decode B1 / KV1 (MHA; o equals the single V row), ragged causal prefill MHA Q16 / KV16, and ragged
 and paged causal prefill GQA4 with queries 32 + 64 at the end of keys
 256 + 1024 (bottom-right causal alignment, fewer queries than keys).
 """
@@ -11,6 +11,7 @@ import torch
 
 import workloads as W
 from oracle import attention as A
+from oracle import bf16
 from tests.gpu_helpers import assert_attention_close, assert_lse_close, dev, host, host_bits, note
 from tests.lib_loader import ensure_built
 
@@ -36,10 +37,11 @@ def test_decode_b1_kv1_returns_the_single_v_row(layout):
     assert rc == oxa.OXA_OK
     torch.cuda.synchronize()
     assert host(status).tolist() == [0]
-    # one key: softmax weight 1, so o is that key's V row, bit for bit
+    # one key: softmax weight 1, so o is that key's V row exactly (in value:
+    # the accumulator starts at +0, so a -0 element comes out as +0)
     page = int(kv.page_indices[0])
     vrow = kv.v_pool[page, 0] if layout == "NHD" else kv.v_pool[page, :, 0]
-    assert np.array_equal(host_bits(o)[0], vrow)
+    assert np.array_equal(bf16.to_f64(host_bits(o)[0]), bf16.to_f64(vrow))
     o_ref, lse_ref = A.paged_decode(case.q, kv.k_pool, kv.v_pool, layout, kv.page_indptr,
                                     kv.page_indices, kv.seq_lens, case.sm_scale)
     assert_lse_close(host(lse), lse_ref)
