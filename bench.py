@@ -285,15 +285,25 @@ def bench_pages_shapes(torch, oxa, W, iters=200, warmup=20):
         q, *args, o, max_seq_len=1, sm_scale=c.sm_scale, layout=kv.layout,
         num_kv_heads=kv.num_kv_heads)))
 
+    # prefill calls pass the optional workspace, with which small calls split
+    # their keys over more CUs; the "_unsplit" rows time the same calls without
+    def workspace(nbytes):
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+
     for name, rc_ in (("ragged_mha_q16_kv16", W.pages_ragged_mha_q16()),
                       ("ragged_gqa4_q32+64_kv256+1024", W.pages_ragged_gqa4())):
         qr, kr, vr = dev(rc_.q), dev(rc_.k), dev(rc_.v)
         orr = torch.empty_like(qr)
         qi, ki = dev(rc_.qo_indptr), dev(rc_.kv_indptr)
         mq, mk = int(np.diff(rc_.qo_indptr).max()), int(np.diff(rc_.kv_indptr).max())
-        timed(name, lambda i, qr=qr, kr=kr, vr=vr, orr=orr, qi=qi, ki=ki, mq=mq, mk=mk, c=rc_:
-              check(oxa.oxa_ragged_prefill(qr, kr, vr, qi, ki, orr, max_qo_len=mq,
-                                           max_kv_len=mk, sm_scale=c.sm_scale, causal=True)))
+        ws = workspace(oxa.oxa_ragged_prefill_workspace_bytes(len(rc_.qo_indptr) - 1,
+                                                              qr.shape[0], qr.shape[1]))
+        for suffix, w in (("", ws), ("_unsplit", None)):
+            timed(name + suffix,
+                  lambda i, qr=qr, kr=kr, vr=vr, orr=orr, qi=qi, ki=ki, mq=mq, mk=mk, c=rc_, w=w:
+                  check(oxa.oxa_ragged_prefill(qr, kr, vr, qi, ki, orr, max_qo_len=mq,
+                                               max_kv_len=mk, sm_scale=c.sm_scale, causal=True,
+                                               workspace=w)))
 
     pc = W.pages_paged_gqa4()
     kv = pc.kv
@@ -301,9 +311,11 @@ def bench_pages_shapes(torch, oxa, W, iters=200, warmup=20):
     op = torch.empty_like(qp)
     pargs = (dev(pc.qo_indptr), dev(kv.k_pool), dev(kv.v_pool), dev(kv.page_indptr),
              dev(kv.page_indices), dev(kv.seq_lens))
-    timed("paged_gqa4_q32+64_kv256+1024", lambda i: check(oxa.oxa_paged_prefill(
-        qp, *pargs, op, max_qo_len=64, max_seq_len=1024, sm_scale=pc.sm_scale,
-        layout=kv.layout, num_kv_heads=kv.num_kv_heads, causal=True)))
+    ws = workspace(oxa.oxa_paged_prefill_workspace_bytes(2, qp.shape[0], qp.shape[1]))
+    for suffix, w in (("", ws), ("_unsplit", None)):
+        timed("paged_gqa4_q32+64_kv256+1024" + suffix, lambda i, w=w: check(oxa.oxa_paged_prefill(
+            qp, *pargs, op, max_qo_len=64, max_seq_len=1024, sm_scale=pc.sm_scale,
+            layout=kv.layout, num_kv_heads=kv.num_kv_heads, causal=True, workspace=w)))
     return res
 
 

@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define OXA_ABI_VERSION 4
+#define OXA_ABI_VERSION 5
 #define OXA_PAGE_SIZE 16
 #define OXA_HEAD_DIM 128
 
@@ -224,7 +224,17 @@ size_t oxa_paged_decode_workspace_bytes(int32_t batch, int32_t num_qo_heads, int
  *
  * Shapes: q, o [nnz_qo][num_qo_heads][128]; k, v [nnz_kv][num_kv_heads][128];
  * lse [nnz_qo][num_qo_heads] or NULL; qo_indptr, kv_indptr [batch+1].
- * The workspace is reserved (the size query returns 0; pass NULL, 0).
+ *
+ * Workspace (optional; NULL disables what follows): a call too small to fill
+ * the GPU - at most nnz_qo * num_qo_heads = 32768 query rows times heads, and
+ * few enough (query tile, kv head) items to leave at least half of the compute
+ * units idle - may cut each item's keys into up to 8 chunks that run in
+ * parallel, and merge their states as the split-K decode does (same
+ * attention up to f32 rounding order).  That needs a workspace of
+ * oxa_ragged_prefill_workspace_bytes(...) bytes (16-byte aligned, any
+ * contents, used for the call only; the query returns 0 for calls too large
+ * to split, whose workspace is then unused).  With the split, rows of o
+ * outside every valid sequence are unspecified.
  * Ranges: 1 <= batch, 0 <= nnz_qo, nnz_kv; 1 <= max_kv_len;
  * 1 <= max_qo_len <= 4096 * BM, where BM = 256 / min(Hq / Hkv, 256) query
  * rows form one tile (for example 262144 rows for four q heads per kv head).
@@ -239,6 +249,8 @@ oxa_status oxa_ragged_prefill(
     void* workspace, size_t workspace_bytes,
     uint16_t* o, float* lse, int32_t* status);
 
+/* Workspace bytes that let oxa_ragged_prefill split small calls' keys (0 when
+ * nnz_qo * num_qo_heads exceeds 32768 or the arguments are invalid). */
 size_t oxa_ragged_prefill_workspace_bytes(int32_t batch, int32_t nnz_qo, int32_t num_qo_heads,
                                           int32_t head_dim);
 
@@ -257,7 +269,7 @@ size_t oxa_ragged_prefill_workspace_bytes(int32_t batch, int32_t nnz_qo, int32_t
  *
  * Shapes: q, o [nnz_qo][num_qo_heads][128]; lse [nnz_qo][num_qo_heads] or
  * NULL; qo_indptr, page_indptr [batch+1]; seq_lens [batch].
- * The workspace is reserved (the size query returns 0; pass NULL, 0).
+ * Workspace as for oxa_ragged_prefill (size: oxa_paged_prefill_workspace_bytes).
  * Ranges as for oxa_ragged_prefill, with max_seq_len in place of max_kv_len.
  */
 oxa_status oxa_paged_prefill(
@@ -272,6 +284,7 @@ oxa_status oxa_paged_prefill(
     void* workspace, size_t workspace_bytes,
     uint16_t* o, float* lse, int32_t* status);
 
+/* As oxa_ragged_prefill_workspace_bytes, for oxa_paged_prefill. */
 size_t oxa_paged_prefill_workspace_bytes(int32_t batch, int32_t nnz_qo, int32_t num_qo_heads,
                                          int32_t head_dim);
 

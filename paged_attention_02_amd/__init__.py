@@ -222,21 +222,37 @@ def oxa_paged_decode(q, k_pages, v_pages, page_indptr, page_indices, seq_lens, o
         _i32(status, "status"))
 
 
+def oxa_ragged_prefill_workspace_bytes(batch, nnz_qo, num_qo_heads, head_dim=HEAD_DIM) -> int:
+    return int(lib().oxa_ragged_prefill_workspace_bytes(batch, nnz_qo, num_qo_heads, head_dim))
+
+
+def oxa_paged_prefill_workspace_bytes(batch, nnz_qo, num_qo_heads, head_dim=HEAD_DIM) -> int:
+    return int(lib().oxa_paged_prefill_workspace_bytes(batch, nnz_qo, num_qo_heads, head_dim))
+
+
+def _ws(workspace):
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
 def oxa_ragged_prefill(q, k, v, qo_indptr, kv_indptr, o, *, max_qo_len, max_kv_len, sm_scale,
-                       causal=True, lse=None, status=None, stream=None) -> int:
-    """Ragged prefill: q/o [nnz_qo, Hq, 128]; k/v [nnz_kv, Hkv, 128]."""
+                       causal=True, lse=None, status=None, workspace=None, stream=None) -> int:
+    """Ragged prefill: q/o [nnz_qo, Hq, 128]; k/v [nnz_kv, Hkv, 128].  With a
+    ``workspace`` of oxa_ragged_prefill_workspace_bytes(...) bytes, small calls
+    split their keys over more CUs."""
     return lib().oxa_ragged_prefill(
         _stream(stream), _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"),
         _i32(qo_indptr, "qo_indptr"), _i32(kv_indptr, "kv_indptr"), qo_indptr.shape[0] - 1,
         q.shape[0], k.shape[0], q.shape[1], k.shape[1], q.shape[2], int(max_qo_len),
-        int(max_kv_len), int(bool(causal)), float(sm_scale), None, 0, _bf16(o, "o"),
+        int(max_kv_len), int(bool(causal)), float(sm_scale), _ptr(workspace), _ws(workspace),
+        _bf16(o, "o"),
         _f32(lse, "lse"), _i32(status, "status"))
 
 
 def oxa_paged_prefill(q, qo_indptr, k_pages, v_pages, page_indptr, page_indices, seq_lens, o, *,
                       max_qo_len, max_seq_len, sm_scale, layout="NHD", num_kv_heads=None,
-                      causal=True, lse=None, status=None, stream=None) -> int:
-    """Paged prefill: q/o [nnz_qo, Hq, 128] over the paged K/V of each sequence."""
+                      causal=True, lse=None, status=None, workspace=None, stream=None) -> int:
+    """Paged prefill: q/o [nnz_qo, Hq, 128] over the paged K/V of each sequence
+    (``workspace`` as for oxa_ragged_prefill)."""
     lay = _layout(layout)
     if num_kv_heads is None:
         num_kv_heads = k_pages.shape[2] if lay == 0 else k_pages.shape[1]
@@ -246,7 +262,8 @@ def oxa_paged_prefill(q, qo_indptr, k_pages, v_pages, page_indptr, page_indices,
         _i32(page_indptr, "page_indptr"), _i32(page_indices, "page_indices"),
         page_indices.shape[0], _i32(seq_lens, "seq_lens"), qo_indptr.shape[0] - 1, q.shape[0],
         q.shape[1], num_kv_heads, q.shape[2], int(max_qo_len), int(max_seq_len),
-        int(bool(causal)), float(sm_scale), None, 0, _bf16(o, "o"), _f32(lse, "lse"),
+        int(bool(causal)), float(sm_scale), _ptr(workspace), _ws(workspace), _bf16(o, "o"),
+        _f32(lse, "lse"),
         _i32(status, "status"))
 
 

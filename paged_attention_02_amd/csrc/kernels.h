@@ -61,7 +61,16 @@ struct PrefillLaunch {
   int32_t paged, layout, batch, nnz_qo, nnz_kv, hq, hkv, max_qo_len, max_kv_len, causal;
   int32_t num_pages, num_page_entries;
   float sm_scale;
+  // key-range split of small calls: chunk states [max_split][nnz_qo][hq][128]
+  // f32 and their lse [max_split][nnz_qo][hq]; max_split <= 1 disables it
+  float* ws_o;
+  float* ws_lse;
+  int32_t max_split;
 };
+// Largest key-range split, and the largest nnz_qo * hq a split call may have
+// (its workspace grows with both).
+constexpr int kPrefillMaxSplit = 8;
+constexpr int64_t kPrefillSplitMaxRowHeads = 1 << 15;
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream);
 
 // Attention-state merge over (row, head) units.  State s of unit (row, h)

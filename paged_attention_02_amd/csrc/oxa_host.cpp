@@ -144,6 +144,41 @@ oxa_status rope_setup(const uint16_t* q_in, uint16_t* q_out, int32_t num_qo_head
   return OXA_OK;
 }
 
+// Prefill workspace for the key-range split of small calls: the chunk states
+// (f32 [kPrefillMaxSplit][nnz_qo][hq][128]) then their lse, 256-byte aligned;
+// 0 when the call is too large to split.
+uint64_t prefill_split_o_bytes(int32_t nnz_qo, int32_t hq) {
+  return ((uint64_t)oxa::kPrefillMaxSplit * nnz_qo * hq * OXA_HEAD_DIM * 4 + 255) / 256 * 256;
+}
+
+size_t prefill_split_bytes(int32_t batch, int32_t nnz_qo, int32_t hq, int32_t head_dim) {
+  if (batch < 1 || nnz_qo < 1 || hq < 1 || head_dim != OXA_HEAD_DIM ||
+      (int64_t)nnz_qo * hq > oxa::kPrefillSplitMaxRowHeads)
+    return 0;
+  return (size_t)(prefill_split_o_bytes(nnz_qo, hq) +
+                  (uint64_t)oxa::kPrefillMaxSplit * nnz_qo * hq * 4);
+}
+
+// Workspace checks shared by both prefills; fills the split fields.
+oxa_status prefill_workspace(int32_t batch, int32_t nnz_qo, int32_t hq, void* workspace,
+                             size_t workspace_bytes, oxa::PrefillLaunch* a, Region* region) {
+  a->ws_o = nullptr;
+  a->ws_lse = nullptr;
+  a->max_split = 1;
+  *region = Region{nullptr, 0};
+  if (workspace == nullptr) return OXA_OK;
+  if (!aligned(workspace, 16)) return OXA_ERR_ALIGN;
+  const size_t need = prefill_split_bytes(batch, nnz_qo, hq, OXA_HEAD_DIM);
+  if (need == 0) return OXA_OK;  // too large to split: the workspace is not used
+  if (workspace_bytes < need) return OXA_ERR_WORKSPACE;
+  unsigned char* w = static_cast<unsigned char*>(workspace);
+  a->ws_o = reinterpret_cast<float*>(w);
+  a->ws_lse = reinterpret_cast<float*>(w + prefill_split_o_bytes(nnz_qo, hq));
+  a->max_split = oxa::kPrefillMaxSplit;
+  *region = Region{workspace, need};
+  return OXA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -336,8 +371,14 @@ oxa_status oxa_paged_decode(hipStream_t stream, const uint16_t* q, int32_t batch
 
 // ---------------------------------------------------------------- prefill
 
-size_t oxa_ragged_prefill_workspace_bytes(int32_t, int32_t, int32_t, int32_t) { return 0; }
-size_t oxa_paged_prefill_workspace_bytes(int32_t, int32_t, int32_t, int32_t) { return 0; }
+size_t oxa_ragged_prefill_workspace_bytes(int32_t batch, int32_t nnz_qo, int32_t num_qo_heads,
+                                          int32_t head_dim) {
+  return prefill_split_bytes(batch, nnz_qo, num_qo_heads, head_dim);
+}
+size_t oxa_paged_prefill_workspace_bytes(int32_t batch, int32_t nnz_qo, int32_t num_qo_heads,
+                                         int32_t head_dim) {
+  return prefill_split_bytes(batch, nnz_qo, num_qo_heads, head_dim);
+}
 
 
 oxa_status oxa_ragged_prefill(hipStream_t stream, const uint16_t* q, const uint16_t* k,
@@ -347,8 +388,6 @@ oxa_status oxa_ragged_prefill(hipStream_t stream, const uint16_t* q, const uint1
                               int32_t head_dim, int32_t max_qo_len, int32_t max_kv_len,
                               int32_t causal, float sm_scale, void* workspace,
                               size_t workspace_bytes, uint16_t* o, float* lse, int32_t* status) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (!q || !k || !v || !qo_indptr || !kv_indptr || !o) return OXA_ERR_NULL;
   if (oxa_status s = check_heads(num_qo_heads, num_kv_heads, head_dim)) return s;
   if (batch < 1 || batch > kMaxGridYZ || nnz_qo < 0 || nnz_kv < 0 || max_qo_len < 1 ||
@@ -367,12 +406,17 @@ oxa_status oxa_ragged_prefill(hipStream_t stream, const uint16_t* q, const uint1
                         {v, (uint64_t)nnz_kv * num_kv_heads * kRowBytes},
                         {qo_indptr, (B + 1) * 4},
                         {kv_indptr, (B + 1) * 4}};
+  oxa::PrefillLaunch a = {};
+  Region ws;
+  if (oxa_status st = prefill_workspace(batch, nnz_qo, num_qo_heads, workspace, workspace_bytes,
+                                        &a, &ws))
+    return st;
   const Region outs[] = {{o, (uint64_t)nnz_qo * num_qo_heads * kRowBytes},
                          {lse, lse ? (uint64_t)nnz_qo * num_qo_heads * 4 : 0},
-                         {status, status ? B * 4 : 0}};
-  if (any_alias(outs, 3, ins, 5)) return OXA_ERR_ALIAS;
+                         {status, status ? B * 4 : 0},
+                         ws};
+  if (any_alias(outs, 4, ins, 5)) return OXA_ERR_ALIAS;
 
-  oxa::PrefillLaunch a = {};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -404,8 +448,6 @@ oxa_status oxa_paged_prefill(hipStream_t stream, const uint16_t* q, const int32_
                              int32_t max_qo_len, int32_t max_seq_len, int32_t causal,
                              float sm_scale, void* workspace, size_t workspace_bytes,
                              uint16_t* o, float* lse, int32_t* status) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (!q || !qo_indptr || !k_pages || !v_pages || !page_indptr || !page_indices || !seq_lens ||
       !o)
     return OXA_ERR_NULL;
@@ -431,12 +473,17 @@ oxa_status oxa_paged_prefill(hipStream_t stream, const uint16_t* q, const int32_
                         {page_indptr, (B + 1) * 4},
                         {page_indices, (uint64_t)num_page_entries * 4},
                         {seq_lens, B * 4}};
+  oxa::PrefillLaunch a = {};
+  Region ws;
+  if (oxa_status st = prefill_workspace(batch, nnz_qo, num_qo_heads, workspace, workspace_bytes,
+                                        &a, &ws))
+    return st;
   const Region outs[] = {{o, (uint64_t)nnz_qo * num_qo_heads * kRowBytes},
                          {lse, lse ? (uint64_t)nnz_qo * num_qo_heads * 4 : 0},
-                         {status, status ? B * 4 : 0}};
-  if (any_alias(outs, 3, ins, 7)) return OXA_ERR_ALIAS;
+                         {status, status ? B * 4 : 0},
+                         ws};
+  if (any_alias(outs, 4, ins, 7)) return OXA_ERR_ALIAS;
 
-  oxa::PrefillLaunch a = {};
   a.q = q;
   a.k = k_pages;
   a.v = v_pages;

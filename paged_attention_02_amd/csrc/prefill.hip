@@ -62,6 +62,12 @@ struct PrefillParams {
   int32_t batch, nnz_qo, nnz_kv, hq, hkv, group, gwg, bm, head_tiles, num_tiles;
   int32_t max_qo_len, max_kv_len, causal, num_pages, num_page_entries;
   float scale_log2;
+  // split > 1: each item's key tiles are cut into `split` contiguous chunks
+  // whose normalised states go to ws_o [split][nnz_qo][hq][128] and ws_lse
+  // [split][nnz_qo][hq] (natural log) for the merge kernel
+  int32_t split;
+  float* ws_o;
+  float* ws_lse;
 };
 
 struct SeqInfo {
@@ -207,8 +213,11 @@ __device__ __forceinline__ void lds_suffix_sum(int* a, int n, int* tot, int tid)
 // work-group is ever idle, which matters because the hardware dispatches
 // groups in order and round-robin over CUs: a regular pattern of instantly
 // finishing groups would pin the live ones to a fraction of the CUs.
-template <bool PAGED, int LAYOUT>
+// SPLIT selects the key-chunked form at compile time, so the unsplit kernel
+// (long prefill) carries none of its registers or code.
+template <bool PAGED, int LAYOUT, bool SPLIT>
 __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
+  const int split = SPLIT ? p.split : 1;
   __shared__ __align__(16) unsigned char smem[4 * kTileBytes];  // K0, V0, K1, V1
   __shared__ int pids[PAGED ? kPidWin : 1];
   __shared__ int lvl_cnt[kMaxLevels + 1];   // sequences with more than t tiles
@@ -259,7 +268,8 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
   lds_suffix_sum(lvl_before, levels + 1, red, tid);
   const int total_pairs = lvl_before[0];
   const int per_pair = p.hkv * p.head_tiles;
-  const int64_t total_items = (int64_t)total_pairs * per_pair;
+  const int64_t base_items = (int64_t)total_pairs * per_pair;
+  const int64_t total_items = base_items * split;  // key chunk is the slowest index
 
   // Deal items to groups boustrophedon-style in units of 8 consecutive items
   // (same tile index, neighbouring kv heads): even rounds go 0 .. G-1, odd
@@ -271,8 +281,10 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
   const int gw = G >= 8 ? 8 : G;
   for (int64_t round = 0; round * G < total_items; ++round) {
     const int64_t slot = (round & 1) ? (int64_t)(G8 - 1 - gblk) * gw + gsub : (int64_t)blockIdx.x;
-    const int64_t item = round * G + slot;
-    if (item >= total_items) continue;
+    const int64_t item_all = round * G + slot;
+    if (item_all >= total_items) continue;
+    const int chunk = SPLIT ? (int)(item_all / base_items) : 0;
+    const int64_t item = item_all - (int64_t)chunk * base_items;
     const int j = (int)(item / per_pair);
     const int kvh = (int)((item / p.head_tiles) % p.hkv);
     const int ht = (int)(item % p.head_tiles);
@@ -315,6 +327,9 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
   const int offset = si.klen - si.qlen;  // bottom-right causal alignment
   const int kv_end = p.causal ? min(si.klen, r0 + rows_here + offset) : si.klen;
   const int ntiles = (kv_end + kBN - 1) / kBN;
+  // this chunk's key tiles [kt0, kt1) (all of them without a split)
+  const int kt0 = (int)((int64_t)chunk * ntiles / split);
+  const int kt1 = (int)((int64_t)(chunk + 1) * ntiles / split);
 
   // this lane's columns: (row, head) pairs wave*32*kCB + cb*32 + col
   bool col_ok[kCB];
@@ -366,19 +381,21 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
     }
   };
   constexpr int kTilesPerWin = kPidWin * kPage / kBN;
-  int wbase = 0;
-  if (PAGED) stage_pids(0);
+  int wbase = kt0 / kTilesPerWin * kPidWin;  // the page-id window of tile kt0
+  if (PAGED) stage_pids(wbase);
   __syncthreads();
 
-  if (ntiles > 0)
-    issue_tile<PAGED, LAYOUT>(p, si, kvh, 0, wave, lane, pids, wbase, smem, smem + kTileBytes);
+  if (kt1 > kt0) {
+    unsigned char* k0 = smem + (kt0 & 1) * 2 * kTileBytes;
+    issue_tile<PAGED, LAYOUT>(p, si, kvh, kt0, wave, lane, pids, wbase, k0, k0 + kTileBytes);
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int kt = 0; kt < ntiles; ++kt) {
+  for (int kt = kt0; kt < kt1; ++kt) {
     const unsigned char* ks = smem + (kt & 1) * 2 * kTileBytes;
     const unsigned char* vs = ks + kTileBytes;
-    if (PAGED && kt + 1 < ntiles && (kt + 1) % kTilesPerWin == 0) {
+    if (PAGED && kt + 1 < kt1 && (kt + 1) % kTilesPerWin == 0) {
       // the next tile starts a new page-id window (only tile kt+1 uses page
       // ids from here on, and every wave is past its reads of the old window)
       wbase = (kt + 1) / kTilesPerWin * kPidWin;
@@ -386,7 +403,7 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
       stage_pids(wbase);
       __syncthreads();
     }
-    if (kt + 1 < ntiles) {  // tile kt+1 streams into the other buffer meanwhile
+    if (kt + 1 < kt1) {  // tile kt+1 streams into the other buffer meanwhile
       unsigned char* kn = smem + ((kt + 1) & 1) * 2 * kTileBytes;
       issue_tile<PAGED, LAYOUT>(p, si, kvh, kt + 1, wave, lane, pids, wbase, kn, kn + kTileBytes);
     }
@@ -496,7 +513,26 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
     const float ls = pair_sum32(lsum[cb]);
     if (!col_ok[cb]) continue;
     const float inv = ls > 0.f ? 1.f / ls : 0.f;
-    uint16_t* orow = p.o + ((int64_t)(si.q0 + qrow[cb]) * p.hq + head[cb]) * kHeadDim;
+    const int64_t hrow = (int64_t)(si.q0 + qrow[cb]) * p.hq + head[cb];
+    const float lse_val = ls > 0.f ? (m[cb] + __log2f(ls)) * kLn2 : -INFINITY;
+    if (SPLIT) {  // this chunk's normalised state, f32
+      const int64_t srow = (int64_t)chunk * p.nnz_qo * p.hq + hrow;
+      float* wrow = p.ws_o + srow * kHeadDim;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          const int dd = 32 * d + 8 * (r >> 2) + 4 * gi;
+          const u32x4_t w = {__float_as_uint(acc[cb][d][r] * inv),
+                             __float_as_uint(acc[cb][d][r + 1] * inv),
+                             __float_as_uint(acc[cb][d][r + 2] * inv),
+                             __float_as_uint(acc[cb][d][r + 3] * inv)};
+          *reinterpret_cast<u32x4_t*>(wrow + dd) = w;
+        }
+      if (gi == 0) p.ws_lse[srow] = lse_val;
+      continue;
+    }
+    uint16_t* orow = p.o + hrow * kHeadDim;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -507,9 +543,7 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
         w[1] = pack_bf16x2(acc[cb][d][r + 2] * inv, acc[cb][d][r + 3] * inv);
         *reinterpret_cast<u32x2_t*>(orow + dd) = w;
       }
-    if (gi == 0 && p.lse != nullptr)
-      p.lse[(int64_t)(si.q0 + qrow[cb]) * p.hq + head[cb]] =
-          ls > 0.f ? (m[cb] + __log2f(ls)) * kLn2 : -INFINITY;
+    if (gi == 0 && p.lse != nullptr) p.lse[hrow] = lse_val;
   }
   __syncthreads();  // LDS (tiles, page ids, selection) is reused by the next item
   }
@@ -568,6 +602,9 @@ hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream) {
   p.num_pages = a.num_pages;
   p.num_page_entries = a.num_page_entries;
   p.scale_log2 = a.sm_scale * kLog2e;
+  p.split = 1;  // raised below for a small call with the workspace for it
+  p.ws_o = a.ws_o;
+  p.ws_lse = a.ws_lse;
   // one persistent work-group per CU (a multiple of 8, so a kv head's items
   // stay on one XCD), never more than there can be items
   int cus = 0;
@@ -575,17 +612,52 @@ hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int64_t pairs_ub = ((int64_t)a.nnz_qo + p.bm - 1) / p.bm + a.batch;
   const int64_t items_ub = pairs_ub * p.hkv * p.head_tiles;
+  // A call whose items would fill at most half of the CUs cuts each item's
+  // keys into chunks (when the caller gave the workspace for it), so more
+  // CUs work and each walks fewer key tiles in series; at most half as many
+  // chunks as the longest item has key tiles.
+  if (a.max_split > 1 && cus > 0) {
+    int64_t split = a.max_split;
+    const int64_t by_cus = cus / (items_ub > 0 ? items_ub : 1);
+    const int64_t by_keys = ((int64_t)(a.max_kv_len + kBN - 1) / kBN + 1) / 2;
+    if (split > by_cus) split = by_cus;
+    if (split > by_keys) split = by_keys;
+    p.split = split >= 2 ? (int32_t)split : 1;
+  }
   int64_t groups = cus >= 8 ? (cus / 8) * 8 : (cus > 0 ? cus : 1);
-  if (groups > items_ub) groups = items_ub > 0 ? items_ub : 1;
+  if (groups > items_ub * p.split) groups = items_ub > 0 ? items_ub * p.split : 1;
   dim3 grid((unsigned)groups);
   dim3 block(kNW * 64);
+  const bool split = p.split > 1;
+  void (*kernel)(PrefillParams);
   if (!a.paged)
-    hipLaunchKernelGGL((prefill_kernel<false, 0>), grid, block, 0, stream, p);
+    kernel = split ? prefill_kernel<false, 0, true> : prefill_kernel<false, 0, false>;
   else if (a.layout == 0)
-    hipLaunchKernelGGL((prefill_kernel<true, 0>), grid, block, 0, stream, p);
+    kernel = split ? prefill_kernel<true, 0, true> : prefill_kernel<true, 0, false>;
   else
-    hipLaunchKernelGGL((prefill_kernel<true, 1>), grid, block, 0, stream, p);
-  return hipGetLastError();
+    kernel = split ? prefill_kernel<true, 1, true> : prefill_kernel<true, 1, false>;
+  hipLaunchKernelGGL(kernel, grid, block, 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess || p.split == 1) return e;
+  // merge the chunks: ws [split][nnz_qo][hq][128] f32 -> o [nnz_qo][hq][128] bf16
+  MergeLaunch m = {};
+  m.v[0] = a.ws_o;
+  m.lse[0] = a.ws_lse;
+  m.v_row = (int64_t)a.hq * kHeadDim;
+  m.v_head = kHeadDim;
+  m.v_state = (int64_t)a.nnz_qo * a.hq * kHeadDim;
+  m.l_row = a.hq;
+  m.l_head = 1;
+  m.l_state = (int64_t)a.nnz_qo * a.hq;
+  m.units = (int64_t)a.nnz_qo * a.hq;
+  m.heads = a.hq;
+  m.states = p.split;
+  m.in_f32 = 1;
+  m.out_f32 = 0;
+  m.pair = 0;
+  m.out = a.o;
+  m.lse_out = a.lse;
+  return launch_merge_states(m, stream);
 }
 
 }  // namespace oxa

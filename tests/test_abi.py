@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     lib = ensure_built()
-    assert lib.oxa_abi_version() == 4
+    assert lib.oxa_abi_version() == 5
     assert oxa.status_string(0) == "OXA_OK"
     assert oxa.status_string(20) == "OXA_DEV_NOT_EXCLUSIVE"
     assert oxa.status_string(999) == "unknown"
@@ -40,7 +40,12 @@ def test_workspace_queries():
     assert oxa.oxa_paged_decode_workspace_bytes(8, 32, 1) == 0
     # the long MQA workload: 8 x 32 rows x 16 partitions x (128 + 1) floats
     assert oxa.oxa_paged_decode_workspace_bytes(8, 32, 16) == 8 * 32 * 16 * 129 * 4 == 2113536
-    assert oxa.lib().oxa_ragged_prefill_workspace_bytes(4, 7680, 32, 128) == 0
+    assert oxa.lib().oxa_ragged_prefill_workspace_bytes(4, 7680, 32, 128) == 0   # too large to split
+    # small prefill: 8 chunk states of 128 f32 (256-byte aligned) + 8 lse, per (row, head)
+    assert oxa.oxa_ragged_prefill_workspace_bytes(2, 96, 32) == 8 * 96 * 32 * (512 + 4)
+    assert oxa.oxa_paged_prefill_workspace_bytes(1, 1024, 32) == 8 * 1024 * 32 * (512 + 4)
+    assert oxa.oxa_paged_prefill_workspace_bytes(1, 1025, 32) == 0
+    assert oxa.oxa_ragged_prefill_workspace_bytes(1, 5, 3) == 8 * 5 * 3 * 516
     # append: one 8-byte record per check work-group (at most 1024 of them)
     assert oxa.oxa_paged_append_rope_workspace_bytes(32768) == 8192
     assert oxa.oxa_paged_append_rope_workspace_bytes(0) == 8192

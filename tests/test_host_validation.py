@@ -82,6 +82,10 @@ def call_ragged(**over):
     (dict(v=addr(2) + 4), oxa.OXA_ERR_ALIGN),
     (dict(o=addr(1) + 256), oxa.OXA_ERR_ALIAS),      # o overlaps k
     (dict(status=addr(4)), oxa.OXA_ERR_ALIAS),       # status over kv_indptr
+    (dict(ws=addr(8) + 4, ws_bytes=1 << 24), oxa.OXA_ERR_ALIGN),
+    (dict(ws=addr(8), ws_bytes=8 * 100 * 8 * 516 - 1), oxa.OXA_ERR_WORKSPACE),
+    (dict(ws=addr(5) - 4096, ws_bytes=1 << 24), oxa.OXA_ERR_ALIAS),    # runs into o
+    (dict(ws=addr(0), ws_bytes=1 << 24), oxa.OXA_ERR_ALIAS),           # over q
 ])
 def test_ragged_rejections(over, code):
     assert call_ragged(**over) == code
@@ -104,6 +108,9 @@ def call_paged_prefill(**over):
     (dict(max_seq=0), oxa.OXA_ERR_SHAPE),
     (dict(o=addr(7) + 2), oxa.OXA_ERR_ALIGN),
     (dict(lse=addr(3) + 8), oxa.OXA_ERR_ALIAS),
+    (dict(ws=addr(9) + 8, ws_bytes=1 << 24), oxa.OXA_ERR_ALIGN),
+    (dict(ws=addr(9), ws_bytes=8 * 50 * 4 * 516 - 4), oxa.OXA_ERR_WORKSPACE),
+    (dict(ws=addr(7), ws_bytes=1 << 24), oxa.OXA_ERR_ALIAS),           # over o
 ])
 def test_paged_prefill_rejections(over, code):
     assert call_paged_prefill(**over) == code
