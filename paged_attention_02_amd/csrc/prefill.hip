@@ -10,26 +10,20 @@
 // Work decomposition (this design): a work-group owns 256 (query row, q head)
 // columns that read the same kv head - BM = 256 / G rows of the G = Hq / Hkv
 // heads of one group - so each K/V tile staged in LDS serves all of them.
-// Four waves (one per SIMD) take 64 columns each, as two 32-column blocks, so
-// every K or V operand fetched from LDS feeds two matrix-core instructions.
-// Per 64-key tile a wave forms S^T = K * Q^T (32 x v_mfma_f32_32x32x16_bf16,
-// K from LDS, Q^T resident in registers), masks only where the tile crosses
-// the causal diagonal or the sequence end, updates the f32 online softmax
-// (lazy rescaling), and accumulates O^T = V^T * P^T (32 more MFMAs; V^T
-// through the LDS transpose read, P^T straight from the score registers).
-// K/V tiles are double-buffered in LDS: the next tile streams from memory
-// straight into the other buffer (no register staging) during the current
-// tile's math.  Tiles are scheduled longest-first: the
-// query-tile index is the slowest grid dimension, counted from the end.
+// Eight waves (two per SIMD) take 32 columns each.  Per 64-key tile a wave
+// forms S^T = K * Q^T (16 x v_mfma_f32_32x32x16_bf16, K from LDS, Q^T resident
+// in registers), masks only where the tile crosses the causal diagonal or the
+// sequence end, updates the f32 online softmax (lazy rescaling), and
+// accumulates O^T = V^T * P^T (16 more MFMAs; V^T through the LDS transpose
+// read, P^T straight from the score registers).  K/V tiles are double-buffered
+// in LDS: the next tile streams from memory straight into the other buffer (no
+// register staging) during the current tile's math.  The grid is persistent
+// (one work-group per CU); every work-group derives the same longest-first
+// list of (sequence, query tile, kv head) items and takes its share of it.
 #include <atomic>
 
 #include "device_common.h"
 #include "kernels.h"
-
-#ifndef PREFILL_NW
-#define PREFILL_NW 8
-#define PREFILL_CB 1
-#endif
 
 namespace oxa {
 namespace {
@@ -40,8 +34,8 @@ constexpr int kStatusSeqLen = 18;
 constexpr int kStatusCausal = 19;
 
 constexpr int kBN = 64;              // keys per tile
-constexpr int kNW = PREFILL_NW;      // waves per work-group
-constexpr int kCB = PREFILL_CB;      // 32-column blocks per wave
+constexpr int kNW = 8;               // waves per work-group
+constexpr int kCB = 1;               // 32-column blocks per wave
 constexpr int kLoadIters = kBN * 16 / (kNW * 64);  // 16-byte K (and V) loads per thread per tile
 constexpr int kCols = kNW * kCB * 32;  // (row, head) columns per work-group
 constexpr int kTileBytes = kBN * 256;  // one K (or V) tile: 64 rows of 256 bytes, swizzled
@@ -120,14 +114,14 @@ __device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
 }
 
 // 16 bytes per lane from global memory straight into LDS at base + 16 * lane
-// (global_load_lds_dwordx4, LDS base in M0).  Written as an instruction the
-// compiler does not track: a tracked one makes it wait for the transfer before
-// the next read of any LDS, which would serialise the load of tile kt+1 with
-// the math on tile kt.  The kernel waits for its transfers itself (vmcnt)
-// before the barrier that hands a buffer to its readers.
+// (global_load_lds_dwordx4, LDS base in M0, which the compiler loads for the
+// operand).  Written as an instruction the compiler does not track: a tracked
+// one makes it wait for the transfer before the next read of any LDS, which
+// would serialise the load of tile kt+1 with the math on tile kt.  The kernel
+// waits for its transfers itself (vmcnt) before the barrier that hands a
+// buffer to its readers.
 __device__ __forceinline__ void dma16(const uint16_t* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(lds_base) : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, off" :: "v"(g), "{m0}"(lds_base) : "memory");
 }
 
 // Bring K/V tile `kt` (64 keys) straight into LDS: wave w fills rows
@@ -413,8 +407,7 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
     // Two online-softmax steps of 32 keys per tile (keeps half the scores live).
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      // S^T[key][col] for keys 32*mb .. +31: 8 k-steps; each K operand read
-      // from LDS serves both column blocks
+      // S^T[key][col] for keys 32*mb .. +31: 8 k-steps over the 128 dims
       f32x16_t s[kCB];
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) s[cb] = f32x16_t{};
@@ -480,8 +473,8 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
         }
         lsum[cb] += psum;
       }
-      // O^T += V^T * P^T over the 2 k-steps of 16 keys in this block; each V^T
-      // operand serves both column blocks.  Transpose read: lanes 4e..4e+3 of
+      // O^T += V^T * P^T over the 2 k-steps of 16 keys in this block.
+      // Transpose read: lanes 4e..4e+3 of
       // a 16-lane group address row (32*mb + 16*h + 4*(l/32) + e) (then +8),
       // 16 dims of the 32-wide d block.
 #pragma unroll
