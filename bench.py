@@ -227,14 +227,31 @@ def bench_append_and_paged_prefill(torch, oxa, case, iters, warmup):
     p_ms = tp.launch_ms(iters)
     torch.cuda.synchronize()
     assert status.cpu().tolist() == [0, -1]
+
+    # the plain append of the same tokens into the same pages (timed last: it
+    # leaves unrotated k in the pages)
+    def plain(i):
+        rc = oxa.oxa_paged_append(k_in, v_in, bi, pos, kp, vp, indptr, ids, rc_t, status,
+                                  layout=kv.layout, workspace=ws_a)
+        if rc != 0:
+            raise RuntimeError(oxa.status_string(rc))
+
+    for i in range(warmup):
+        plain(i)
+    tq = LaunchTimer(torch, stream, iters)
+    tq.run(plain, iters)
+    q_ms = tq.launch_ms(iters)
+    torch.cuda.synchronize()
+    assert status.cpu().tolist() == [0, -1]
     nnz, hq, d = case.q.shape
-    append_bytes = (nnz * hq * d * 2 * 2            # q read + q_out write
-                    + nnz * hkv * d * 2 * 2 * 2     # k, v read + written into pages
-                    + nnz * 4 * 2                   # positions + batch indices
-                    + nnz // 16 * 4 * 2)            # page ids + refcounts, once per page
+    kv_bytes = (nnz * hkv * d * 2 * 2 * 2           # k, v read + written into pages
+                + nnz * 4 * 2                       # positions + batch indices
+                + nnz // 16 * 4 * 2)                # page ids + refcounts, once per page
+    append_bytes = nnz * hq * d * 2 * 2 + kv_bytes  # + q read and q_out written
     qlens = np.diff(case.qo_indptr)
     return dict(append_ms=a_ms, append_bytes=append_bytes, prefill_ms=p_ms,
-                prefill_flops=causal_flops(qlens, kv.seq_lens, hq))
+                prefill_flops=causal_flops(qlens, kv.seq_lens, hq), plain_ms=q_ms,
+                plain_bytes=kv_bytes)
 
 
 def bench_pages_shapes(torch, oxa, W, iters=200, warmup=20):
@@ -550,6 +567,11 @@ def main():
         rows["rope_append_2x16384"] = {"us": round(am * 1e3, 1), "GB/s": round(gbs, 1),
                                        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                                        "bytes": r["append_bytes"]}
+        qm = float(np.mean(r["plain_ms"]))
+        gq = r["plain_bytes"] / (qm * 1e-3) / 1e9
+        rows["plain_append_2x16384"] = {"us": round(qm * 1e3, 1), "GB/s": round(gq, 1),
+                                        "frac_hbm": round(gq / HBM_PEAK_GBS, 4),
+                                        "bytes": r["plain_bytes"]}
         rows["prefill_paged_gqa4_2x16384"] = {"us": round(pm * 1e3, 1), "TFLOPS": round(tf, 1),
                                               "frac_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                                               "flops": r["prefill_flops"]}

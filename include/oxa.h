@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define OXA_ABI_VERSION 5
+#define OXA_ABI_VERSION 6
 #define OXA_PAGE_SIZE 16
 #define OXA_HEAD_DIM 128
 
@@ -161,6 +161,32 @@ oxa_status oxa_paged_append_rope(
 
 /* Workspace bytes oxa_paged_append_rope needs (8192, whatever nnz is). */
 size_t oxa_paged_append_rope_workspace_bytes(int32_t nnz);
+
+/*
+ * Plain paged KV append into exclusively owned pages: k_in[t] and v_in[t] are
+ * stored as they are (no rotation) at slot p % 16 of page
+ * page_indices[page_indptr[b] + p / 16], b = batch_indices[t],
+ * p = positions[t].  ("Oxide Infer" README, "Operator surface": the KV-cache
+ * family lists paged append beside RoPE plus paged append; "FlashInfer parity
+ * matrix", "Domain coverage": paged KV append, the standard append; "Paged KV
+ * ownership difference": writes only pages whose reference count is one.)
+ *
+ * Checks, all-or-nothing behaviour, status[2], workspace, layouts, shapes and
+ * ranges are those of oxa_paged_append_rope without q and without RoPE.
+ */
+oxa_status oxa_paged_append(
+    hipStream_t stream,
+    const uint16_t* k_in, const uint16_t* v_in, int32_t num_kv_heads, int32_t head_dim,
+    const int32_t* batch_indices, const int32_t* positions, int32_t nnz,
+    uint16_t* k_pages, uint16_t* v_pages, int32_t num_pages, int32_t page_size, int32_t layout,
+    const int32_t* page_indptr, int32_t batch,
+    const int32_t* page_indices, int32_t num_page_entries,
+    const int32_t* page_refcounts,
+    void* workspace, size_t workspace_bytes,
+    int32_t* status);
+
+/* Workspace bytes oxa_paged_append needs (as oxa_paged_append_rope). */
+size_t oxa_paged_append_workspace_bytes(int32_t nnz);
 
 /*
  * Paged batch decode: one query token per sequence over its paged KV.

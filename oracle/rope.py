@@ -104,6 +104,44 @@ def append_status(batch_indices, positions, page_indptr, page_indices, page_refc
     return None
 
 
+def paged_append(k_bits, v_bits, batch_indices, positions, k_pool, v_pool, layout,
+                 page_indptr, page_indices, page_refcounts):
+    """Plain paged append ("Oxide Infer" README, "Operator surface": paged append
+    beside RoPE plus paged append): (k, v) rows stored as they are, under the
+    same all-or-nothing exclusive-page rules as the fused op.
+
+    Returns (reason, k_pool_after, v_pool_after); on failure the pools come
+    back unchanged.
+    """
+    batch = len(page_indptr) - 1
+    bad = append_status(batch_indices, positions, page_indptr, page_indices,
+                        page_refcounts, k_pool.shape[0], batch)
+    if bad is not None:
+        return bad[1], k_pool.copy(), v_pool.copy()
+    k_after, v_after = _store(k_bits, v_bits, batch_indices, positions, k_pool, v_pool, layout,
+                              page_indptr, page_indices)
+    return None, k_after, v_after
+
+
+def _store(k_rows, v_rows, batch_indices, positions, k_pool, v_pool, layout, page_indptr,
+           page_indices):
+    """Copies of the pools with token t's rows at (page, slot) of its position."""
+    k_after, v_after = k_pool.copy(), v_pool.copy()
+    for t in range(len(positions)):
+        b, p = int(batch_indices[t]), int(positions[t])
+        page = int(page_indices[int(page_indptr[b]) + p // PAGE_SIZE])
+        slot = p % PAGE_SIZE
+        if layout == "NHD":
+            k_after[page, slot, :, :] = k_rows[t]
+            v_after[page, slot, :, :] = v_rows[t]
+        elif layout == "HND":
+            k_after[page, :, slot, :] = k_rows[t]
+            v_after[page, :, slot, :] = v_rows[t]
+        else:
+            raise ValueError(layout)
+    return k_after, v_after
+
+
 def paged_append_rope(q_bits, k_bits, v_bits, batch_indices, positions, k_pool, v_pool,
                       layout, page_indptr, page_indices, page_refcounts, theta):
     """Fused NeoX RoPE on q and k plus the append of (rotated k, v) into the pages.
@@ -119,17 +157,6 @@ def paged_append_rope(q_bits, k_bits, v_bits, batch_indices, positions, k_pool, 
         return bad[1], None, k_pool.copy(), v_pool.copy()
     q_out = None if q_bits is None else rope_neox_bf16(q_bits, positions, theta)
     k_rot = rope_neox_bf16(k_bits, positions, theta)
-    k_after, v_after = k_pool.copy(), v_pool.copy()
-    for t in range(len(positions)):
-        b, p = int(batch_indices[t]), int(positions[t])
-        page = int(page_indices[int(page_indptr[b]) + p // PAGE_SIZE])
-        slot = p % PAGE_SIZE
-        if layout == "NHD":
-            k_after[page, slot, :, :] = k_rot[t]
-            v_after[page, slot, :, :] = v_bits[t]
-        elif layout == "HND":
-            k_after[page, :, slot, :] = k_rot[t]
-            v_after[page, :, slot, :] = v_bits[t]
-        else:
-            raise ValueError(layout)
+    k_after, v_after = _store(k_rot, v_bits, batch_indices, positions, k_pool, v_pool, layout,
+                              page_indptr, page_indices)
     return None, q_out, k_after, v_after

@@ -54,6 +54,9 @@ SIGNATURES = {
     "oxa_paged_append_rope": (_I, [_P, _P, _P, _I, _P, _P, _I, _I, _P, _P, _I, _P, _P, _I, _I, _I,
                                    _P, _I, _P, _I, _P, _F, _P, _Z, _P]),
     "oxa_paged_append_rope_workspace_bytes": (_Z, [_I]),
+    "oxa_paged_append": (_I, [_P, _P, _P, _I, _I, _P, _P, _I, _P, _P, _I, _I, _I, _P, _I, _P, _I,
+                              _P, _P, _Z, _P]),
+    "oxa_paged_append_workspace_bytes": (_Z, [_I]),
     "oxa_paged_decode": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _P, _P, _I, _P, _I, _F,
                               _I, _P, _Z, _P, _P, _P]),
     "oxa_paged_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
@@ -198,6 +201,30 @@ def oxa_paged_append_rope(q_in, q_out, k_in, v_in, batch_indices, positions, k_p
         page_indptr.shape[0] - 1, _i32(page_indices, "page_indices"), page_indices.shape[0],
         _i32(page_refcounts, "page_refcounts"), float(rope_theta), _ptr(workspace), ws_bytes,
         _i32(status, "status"))
+
+
+def oxa_paged_append_workspace_bytes(nnz) -> int:
+    return int(lib().oxa_paged_append_workspace_bytes(nnz))
+
+
+def oxa_paged_append(k_in, v_in, batch_indices, positions, k_pages, v_pages, page_indptr,
+                     page_indices, page_refcounts, status, *, layout="NHD", workspace=None,
+                     stream=None) -> int:
+    """Plain append of (k, v) rows into exclusive pages, no rotation; arguments
+    as for oxa_paged_append_rope without q and rope_theta."""
+    lay = _layout(layout)
+    if workspace is None:
+        import torch
+        nbytes = oxa_paged_append_workspace_bytes(k_in.shape[0])
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=k_in.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    return lib().oxa_paged_append(
+        _stream(stream), _bf16(k_in, "k_in"), _bf16(v_in, "v_in"), k_in.shape[1], k_in.shape[2],
+        _i32(batch_indices, "batch_indices"), _i32(positions, "positions"), k_in.shape[0],
+        _bf16(k_pages, "k_pages"), _bf16(v_pages, "v_pages"), k_pages.shape[0], PAGE_SIZE, lay,
+        _i32(page_indptr, "page_indptr"), page_indptr.shape[0] - 1,
+        _i32(page_indices, "page_indices"), page_indices.shape[0],
+        _i32(page_refcounts, "page_refcounts"), _ptr(workspace), ws_bytes, _i32(status, "status"))
 
 
 def oxa_paged_decode_workspace_bytes(batch, num_qo_heads, num_partitions, head_dim=HEAD_DIM) -> int:

@@ -1,4 +1,5 @@
-// Fused NeoX RoPE + paged KV append into exclusively owned pages (gfx950).
+// Paged KV append into exclusively owned pages, fused with NeoX RoPE of k (and
+// q) or plain (gfx950).
 //
 // Operator contract: "FlashInfer parity matrix", section "Admitted attention
 // matrix" (rows Standard RoPE - D128 NeoX split-half with explicit I32
@@ -6,7 +7,9 @@
 // reference counts) and section "Paged KV ownership difference" (append takes
 // an authoritative reference-count snapshot and writes only pages whose count
 // is one); "Oxide Infer" README, section "Operator surface" (BF16 NeoX RoPE
-// with explicit positions; RoPE plus paged append).
+// with explicit positions; paged append and RoPE plus paged append); "FlashInfer
+// parity matrix", section "Domain coverage" (paged KV append: the standard
+// append beside the fused RoPE one).
 //
 // Two kernels keep the call all-or-nothing without a host round trip:
 //  1. the check pass: each work-group validates a share of the tokens and
@@ -145,11 +148,12 @@ __global__ __launch_bounds__(256) void append_check_kernel(AppendParams p) {
   }
 }
 
-// Grid-stride over tokens, one wave per token at a time.  Lane l evaluates
-// the sin/cos of frequency l and shares it through a wave-private LDS slot;
-// lane l then rotates the frequency chunk f = l % 8 (frequencies 8f .. 8f+7)
-// of every head it handles.
-template <int LAYOUT>
+// Grid-stride over tokens, one wave per token at a time.  With ROPE, lane l
+// evaluates the sin/cos of frequency l and shares it through a wave-private
+// LDS slot; lane l then rotates the frequency chunk f = l % 8 (frequencies
+// 8f .. 8f+7) of every head it handles.  Without ROPE (the plain append) K is
+// copied like V.
+template <int LAYOUT, bool ROPE>
 __global__ __launch_bounds__(256) void append_rope_kernel(AppendParams p) {
   __shared__ double cs[4][64][2];
   __shared__ int g_bad, g_code;
@@ -180,6 +184,22 @@ __global__ __launch_bounds__(256) void append_rope_kernel(AppendParams p) {
     if (check_token(p, t, &page) != 0) continue;  // cannot happen after the check
     const int pos = p.positions[t];
     const int slot = pos & (kPage - 1);
+    const uint16_t* ki = p.k_in + (int64_t)t * p.hkv * kHeadDim;
+    const uint16_t* vi = p.v_in + (int64_t)t * p.hkv * kHeadDim;
+    if constexpr (!ROPE) {
+      // plain append: K and V rows as they are, 16-byte chunks, 16 per head
+      for (int cidx = lane; cidx < p.hkv * 16; cidx += 64) {
+        const int h = cidx >> 4;
+        const int ch = cidx & 15;
+        const u32x4_t wk = ldg16(ki + h * kHeadDim + 8 * ch);
+        const u32x4_t wv = ldg16(vi + h * kHeadDim + 8 * ch);
+        const int64_t row = LAYOUT == 0 ? (((int64_t)page * kPage + slot) * p.hkv + h) * kHeadDim
+                                        : (((int64_t)page * p.hkv + h) * kPage + slot) * kHeadDim;
+        *reinterpret_cast<u32x4_t*>(p.kp + row + 8 * ch) = wk;
+        *reinterpret_cast<u32x4_t*>(p.vp + row + 8 * ch) = wv;
+      }
+      continue;
+    }
     {
       double sl, cl;
       sincos((double)pos * p.inv_freq[lane], &sl, &cl);
@@ -204,8 +224,6 @@ __global__ __launch_bounds__(256) void append_rope_kernel(AppendParams p) {
         *reinterpret_cast<u32x4_t*>(qo + h * kHeadDim + 64 + 8 * f) = o2;
       }
     }
-    const uint16_t* ki = p.k_in + (int64_t)t * p.hkv * kHeadDim;
-    const uint16_t* vi = p.v_in + (int64_t)t * p.hkv * kHeadDim;
     for (int h = hsub; h < p.hkv; h += 8) {
       const u32x4_t w1 = ldg16(ki + h * kHeadDim + 8 * f);
       const u32x4_t w2 = ldg16(ki + h * kHeadDim + 64 + 8 * f);
@@ -267,10 +285,11 @@ hipError_t launch_paged_append_rope(const AppendLaunch& a, hipStream_t stream) {
   int blocks = (a.nnz + 3) / 4;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
-  if (a.layout == 0)
-    hipLaunchKernelGGL(append_rope_kernel<0>, dim3(blocks), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(append_rope_kernel<1>, dim3(blocks), dim3(256), 0, stream, p);
+  void (*kernel)(AppendParams) = a.rope ? (a.layout == 0 ? append_rope_kernel<0, true>
+                                                           : append_rope_kernel<1, true>)
+                                        : (a.layout == 0 ? append_rope_kernel<0, false>
+                                                         : append_rope_kernel<1, false>);
+  hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -39,6 +39,7 @@ struct AppendLaunch {
   int32_t* status;
   int32_t* check;  // workspace: [kAppendCheckGroups][2] per-work-group check records
   int32_t hq, hkv, nnz, num_pages, layout, batch, num_page_entries;
+  int32_t rope;         // 1: k is stored rotated (and q rotated if given); 0: k stored as is
   double inv_freq[64];  // rope_theta^(-2i/128), i < 64, computed on the host in double
 };
 // Work-groups of the append check pass, at most: the workspace holds one

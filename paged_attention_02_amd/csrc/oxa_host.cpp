@@ -179,50 +179,17 @@ oxa_status prefill_workspace(int32_t batch, int32_t nnz_qo, int32_t hq, void* wo
   return OXA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int32_t oxa_abi_version(void) { return OXA_ABI_VERSION; }
-
-const char* oxa_status_string(int32_t code) {
-  switch (code) {
-    case OXA_OK: return "OXA_OK";
-    case OXA_ERR_NULL: return "OXA_ERR_NULL";
-    case OXA_ERR_UNSUPPORTED: return "OXA_ERR_UNSUPPORTED";
-    case OXA_ERR_SHAPE: return "OXA_ERR_SHAPE";
-    case OXA_ERR_ALIGN: return "OXA_ERR_ALIGN";
-    case OXA_ERR_ALIAS: return "OXA_ERR_ALIAS";
-    case OXA_ERR_WORKSPACE: return "OXA_ERR_WORKSPACE";
-    case OXA_ERR_LAUNCH: return "OXA_ERR_LAUNCH";
-    case OXA_DEV_PAGE_RANGE: return "OXA_DEV_PAGE_RANGE";
-    case OXA_DEV_INDPTR: return "OXA_DEV_INDPTR";
-    case OXA_DEV_SEQ_LEN: return "OXA_DEV_SEQ_LEN";
-    case OXA_DEV_CAUSAL: return "OXA_DEV_CAUSAL";
-    case OXA_DEV_NOT_EXCLUSIVE: return "OXA_DEV_NOT_EXCLUSIVE";
-    case OXA_DEV_CAPACITY: return "OXA_DEV_CAPACITY";
-    case OXA_DEV_BATCH_INDEX: return "OXA_DEV_BATCH_INDEX";
-    default: return "unknown";
-  }
-}
-
-// ---------------------------------------------------------------- append
-
-size_t oxa_paged_append_rope_workspace_bytes(int32_t nnz) {
-  (void)nnz;  // one record per check work-group, whatever the token count
-  return (size_t)oxa::kAppendCheckGroups * 8;
-}
-
-oxa_status oxa_paged_append_rope(hipStream_t stream, const uint16_t* q_in, uint16_t* q_out,
-                                 int32_t num_qo_heads, const uint16_t* k_in,
-                                 const uint16_t* v_in, int32_t num_kv_heads, int32_t head_dim,
-                                 const int32_t* batch_indices, const int32_t* positions,
-                                 int32_t nnz, uint16_t* k_pages, uint16_t* v_pages,
-                                 int32_t num_pages, int32_t page_size, int32_t layout,
-                                 const int32_t* page_indptr, int32_t batch,
-                                 const int32_t* page_indices, int32_t num_page_entries,
-                                 const int32_t* page_refcounts, float rope_theta,
-                                 void* workspace, size_t workspace_bytes, int32_t* status) {
+// Both paged appends: validation, then the check pass and the writer.
+oxa_status paged_append_impl(hipStream_t stream, const uint16_t* q_in, uint16_t* q_out,
+                             int32_t num_qo_heads, const uint16_t* k_in,
+                             const uint16_t* v_in, int32_t num_kv_heads, int32_t head_dim,
+                             const int32_t* batch_indices, const int32_t* positions,
+                             int32_t nnz, uint16_t* k_pages, uint16_t* v_pages,
+                             int32_t num_pages, int32_t page_size, int32_t layout,
+                             const int32_t* page_indptr, int32_t batch,
+                             const int32_t* page_indices, int32_t num_page_entries,
+                             const int32_t* page_refcounts, bool rope, float rope_theta,
+                             void* workspace, size_t workspace_bytes, int32_t* status) {
   // with no tokens the per-token arrays may be absent (empty tensors)
   if ((nnz != 0 && (!k_in || !v_in || !batch_indices || !positions)) || !k_pages || !v_pages ||
       !page_indptr || !page_indices || !page_refcounts || !status)
@@ -233,13 +200,13 @@ oxa_status oxa_paged_append_rope(hipStream_t stream, const uint16_t* q_in, uint1
   if (num_kv_heads < 1 || (has_q && num_qo_heads < 1)) return OXA_ERR_SHAPE;
   if (oxa_status s = check_paging(page_size, layout, num_pages, num_page_entries)) return s;
   if (nnz < 0 || batch < 1) return OXA_ERR_SHAPE;
-  if (!(rope_theta > 0.f) || !std::isfinite(rope_theta)) return OXA_ERR_SHAPE;
+  if (rope && (!(rope_theta > 0.f) || !std::isfinite(rope_theta))) return OXA_ERR_SHAPE;
   if (!aligned(q_in, 16) || !aligned(q_out, 16) || !aligned(k_in, 16) || !aligned(v_in, 16) ||
       !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(batch_indices, 4) ||
       !aligned(positions, 4) || !aligned(page_indptr, 4) || !aligned(page_indices, 4) ||
       !aligned(page_refcounts, 4) || !aligned(status, 4) || !aligned(workspace, 16))
     return OXA_ERR_ALIGN;
-  const size_t need = oxa_paged_append_rope_workspace_bytes(nnz);
+  const size_t need = (size_t)oxa::kAppendCheckGroups * 8;
   if (workspace == nullptr || workspace_bytes < need) return OXA_ERR_WORKSPACE;
 
   const uint64_t n = (uint64_t)nnz;
@@ -287,9 +254,79 @@ oxa_status oxa_paged_append_rope(hipStream_t stream, const uint16_t* q_in, uint1
   a.layout = layout;
   a.batch = batch;
   a.num_page_entries = num_page_entries;
+  a.rope = rope ? 1 : 0;
   for (int i = 0; i < 64; ++i)
-    a.inv_freq[i] = std::pow((double)rope_theta, -2.0 * (double)i / (double)OXA_HEAD_DIM);
+    a.inv_freq[i] =
+        rope ? std::pow((double)rope_theta, -2.0 * (double)i / (double)OXA_HEAD_DIM) : 0.0;
   return launch_status(oxa::launch_paged_append_rope(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t oxa_abi_version(void) { return OXA_ABI_VERSION; }
+
+const char* oxa_status_string(int32_t code) {
+  switch (code) {
+    case OXA_OK: return "OXA_OK";
+    case OXA_ERR_NULL: return "OXA_ERR_NULL";
+    case OXA_ERR_UNSUPPORTED: return "OXA_ERR_UNSUPPORTED";
+    case OXA_ERR_SHAPE: return "OXA_ERR_SHAPE";
+    case OXA_ERR_ALIGN: return "OXA_ERR_ALIGN";
+    case OXA_ERR_ALIAS: return "OXA_ERR_ALIAS";
+    case OXA_ERR_WORKSPACE: return "OXA_ERR_WORKSPACE";
+    case OXA_ERR_LAUNCH: return "OXA_ERR_LAUNCH";
+    case OXA_DEV_PAGE_RANGE: return "OXA_DEV_PAGE_RANGE";
+    case OXA_DEV_INDPTR: return "OXA_DEV_INDPTR";
+    case OXA_DEV_SEQ_LEN: return "OXA_DEV_SEQ_LEN";
+    case OXA_DEV_CAUSAL: return "OXA_DEV_CAUSAL";
+    case OXA_DEV_NOT_EXCLUSIVE: return "OXA_DEV_NOT_EXCLUSIVE";
+    case OXA_DEV_CAPACITY: return "OXA_DEV_CAPACITY";
+    case OXA_DEV_BATCH_INDEX: return "OXA_DEV_BATCH_INDEX";
+    default: return "unknown";
+  }
+}
+
+// ---------------------------------------------------------------- append
+
+size_t oxa_paged_append_rope_workspace_bytes(int32_t nnz) {
+  (void)nnz;  // one record per check work-group, whatever the token count
+  return (size_t)oxa::kAppendCheckGroups * 8;
+}
+
+oxa_status oxa_paged_append_rope(hipStream_t stream, const uint16_t* q_in, uint16_t* q_out,
+                                 int32_t num_qo_heads, const uint16_t* k_in,
+                                 const uint16_t* v_in, int32_t num_kv_heads, int32_t head_dim,
+                                 const int32_t* batch_indices, const int32_t* positions,
+                                 int32_t nnz, uint16_t* k_pages, uint16_t* v_pages,
+                                 int32_t num_pages, int32_t page_size, int32_t layout,
+                                 const int32_t* page_indptr, int32_t batch,
+                                 const int32_t* page_indices, int32_t num_page_entries,
+                                 const int32_t* page_refcounts, float rope_theta,
+                                 void* workspace, size_t workspace_bytes, int32_t* status) {
+  return paged_append_impl(stream, q_in, q_out, num_qo_heads, k_in, v_in, num_kv_heads, head_dim,
+                           batch_indices, positions, nnz, k_pages, v_pages, num_pages, page_size,
+                           layout, page_indptr, batch, page_indices, num_page_entries,
+                           page_refcounts, true, rope_theta, workspace, workspace_bytes, status);
+}
+
+size_t oxa_paged_append_workspace_bytes(int32_t nnz) {
+  return oxa_paged_append_rope_workspace_bytes(nnz);
+}
+
+oxa_status oxa_paged_append(hipStream_t stream, const uint16_t* k_in, const uint16_t* v_in,
+                            int32_t num_kv_heads, int32_t head_dim, const int32_t* batch_indices,
+                            const int32_t* positions, int32_t nnz, uint16_t* k_pages,
+                            uint16_t* v_pages, int32_t num_pages, int32_t page_size,
+                            int32_t layout, const int32_t* page_indptr, int32_t batch,
+                            const int32_t* page_indices, int32_t num_page_entries,
+                            const int32_t* page_refcounts, void* workspace,
+                            size_t workspace_bytes, int32_t* status) {
+  return paged_append_impl(stream, nullptr, nullptr, 0, k_in, v_in, num_kv_heads, head_dim,
+                           batch_indices, positions, nnz, k_pages, v_pages, num_pages, page_size,
+                           layout, page_indptr, batch, page_indices, num_page_entries,
+                           page_refcounts, false, 0.f, workspace, workspace_bytes, status);
 }
 
 // ---------------------------------------------------------------- decode

@@ -19,7 +19,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = ensure_built()
     names = declared_functions()
-    assert {"oxa_paged_append_rope", "oxa_paged_decode", "oxa_ragged_prefill",
+    assert {"oxa_paged_append_rope", "oxa_paged_append", "oxa_paged_decode", "oxa_ragged_prefill",
             "oxa_paged_prefill", "oxa_merge_states", "oxa_merge_state_pair", "oxa_rope_neox",
             "oxa_rope_llama31"} <= set(names)
     for n in names:
@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     lib = ensure_built()
-    assert lib.oxa_abi_version() == 5
+    assert lib.oxa_abi_version() == 6
     assert oxa.status_string(0) == "OXA_OK"
     assert oxa.status_string(20) == "OXA_DEV_NOT_EXCLUSIVE"
     assert oxa.status_string(999) == "unknown"
@@ -49,3 +49,4 @@ def test_workspace_queries():
     # append: one 8-byte record per check work-group (at most 1024 of them)
     assert oxa.oxa_paged_append_rope_workspace_bytes(32768) == 8192
     assert oxa.oxa_paged_append_rope_workspace_bytes(0) == 8192
+    assert oxa.oxa_paged_append_workspace_bytes(32768) == 8192

@@ -170,3 +170,72 @@ def test_rope_append_full_size():
     d = ulp_diff(got["q_out"], q_ref)
     assert d.max() <= 1, "q differs by more than one bf16 ulp"
     assert np.count_nonzero(d) == 0, f"{np.count_nonzero(d)} q values differ by 1 ulp"
+
+
+def run_plain(case, *, refcounts=None, positions=None, kp=None, vp=None):
+    ensure_built()
+    kv = case.kv
+    kp = dev(kv.k_pool) if kp is None else kp
+    vp = dev(kv.v_pool) if vp is None else vp
+    status = torch.full((2,), -7, dtype=torch.int32, device="cuda")
+    code = oxa.oxa_paged_append(dev(case.k), dev(case.v), dev(case.batch_indices),
+                                dev(case.positions if positions is None else positions), kp, vp,
+                                dev(kv.page_indptr), dev(kv.page_indices),
+                                dev(case.page_refcounts if refcounts is None else refcounts),
+                                status, layout=kv.layout)
+    assert code == oxa.OXA_OK, oxa.status_string(code)
+    torch.cuda.synchronize()
+    return host_bits(kp), host_bits(vp), host(status)
+
+
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_plain_append_matches_oracle(layout):
+    case = W.append_case(31, seq_lens=[5, 37, 16, 64, 1], num_qo_heads=8, num_kv_heads=4,
+                         layout=layout, extra_pages=1, spare_pages=5)
+    note(f"plain append {layout}")
+    k, v, status = run_plain(case)
+    kv = case.kv
+    reason, k_ref, v_ref = R.paged_append(case.k, case.v, case.batch_indices, case.positions,
+                                          kv.k_pool, kv.v_pool, layout, kv.page_indptr,
+                                          kv.page_indices, case.page_refcounts)
+    assert reason is None and status.tolist() == [0, -1]
+    assert np.array_equal(k, k_ref) and np.array_equal(v, v_ref)
+
+
+def test_plain_append_rejection_writes_nothing():
+    case = W.append_case(32, seq_lens=[20, 9, 33], num_qo_heads=4, num_kv_heads=2)
+    kv = case.kv
+    rc = case.page_refcounts.copy()
+    rc[kv.page_indices[kv.page_indptr[1]]] = 2      # sequence 1's only page is shared
+    note("plain append with a shared page")
+    k, v, status = run_plain(case, refcounts=rc)
+    reason, _, _ = R.paged_append(case.k, case.v, case.batch_indices, case.positions, kv.k_pool,
+                                  kv.v_pool, kv.layout, kv.page_indptr, kv.page_indices, rc)
+    first_bad = 20                                   # sequence 1's first token
+    assert R.append_status(case.batch_indices, case.positions, kv.page_indptr, kv.page_indices,
+                           rc, kv.num_pages, 3) == (first_bad, "not_exclusive")
+    assert reason == "not_exclusive"
+    assert status.tolist() == [oxa.OXA_DEV_NOT_EXCLUSIVE, first_bad]
+    assert np.array_equal(k, kv.k_pool) and np.array_equal(v, kv.v_pool)
+
+
+def test_plain_append_full_size_and_equal_to_fused_at_position_zero():
+    """The 2 x 16384-token, 8 kv head append shape, every pool bit against the
+    oracle; then one token per sequence at position 0, where the fused RoPE
+    append (angle 0) must store the same bits as the plain one."""
+    case = W.rope_append_prefill()
+    kv = case.kv
+    note("plain append 32768 tokens")
+    k, v, status = run_plain(case)
+    reason, k_ref, v_ref = R.paged_append(case.k, case.v, case.batch_indices, case.positions,
+                                          kv.k_pool, kv.v_pool, kv.layout, kv.page_indptr,
+                                          kv.page_indices, case.page_refcounts)
+    assert reason is None and status.tolist() == [0, -1]
+    assert np.array_equal(k, k_ref) and np.array_equal(v, v_ref)
+    small = W.append_case(33, seq_lens=[1] * 7, num_qo_heads=4, num_kv_heads=8)
+    assert not small.positions.any()
+    note("plain and fused append at position 0")
+    k1, v1, s1 = run_plain(small)
+    got = run_append(small, with_q=False)
+    assert s1.tolist() == [0, -1] and got["status"].tolist() == [0, -1]
+    assert np.array_equal(k1, got["k"]) and np.array_equal(v1, got["v"])

@@ -151,6 +151,31 @@ def test_append_rejections(over, code):
     assert call_append(**over) == code
 
 
+def call_plain_append(**over):
+    args = dict(stream=None, k_in=addr(2), v_in=addr(3), hkv=2, head_dim=128, bidx=addr(4),
+                pos=addr(5), nnz=20, kp=addr(6), vp=addr(7), num_pages=10, page_size=16,
+                layout=1, indptr=addr(8), batch=2, indices=addr(9), num_entries=10,
+                refc=addr(10), ws=addr(12), ws_bytes=8192, status=addr(11))
+    args.update(over)
+    return ensure_built().oxa_paged_append(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(status=None), oxa.OXA_ERR_NULL),
+    (dict(v_in=None), oxa.OXA_ERR_NULL),
+    (dict(head_dim=64), oxa.OXA_ERR_UNSUPPORTED),
+    (dict(layout=2), oxa.OXA_ERR_UNSUPPORTED),
+    (dict(hkv=0), oxa.OXA_ERR_SHAPE),
+    (dict(batch=0), oxa.OXA_ERR_SHAPE),
+    (dict(v_in=addr(3) + 4), oxa.OXA_ERR_ALIGN),
+    (dict(kp=addr(3)), oxa.OXA_ERR_ALIAS),              # K pool over v_in
+    (dict(ws_bytes=100), oxa.OXA_ERR_WORKSPACE),
+    (dict(ws=addr(6) + 512), oxa.OXA_ERR_ALIAS),        # workspace inside the K pool
+])
+def test_plain_append_rejections(over, code):
+    assert call_plain_append(**over) == code
+
+
 def call_merge(**over):
     args = dict(stream=None, v=addr(0), lse=addr(1), v_dtype=0, rows=4, states=3, heads=8,
                 head_dim=128, v_out=addr(2), out_dtype=0, lse_out=addr(3))

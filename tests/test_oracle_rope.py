@@ -190,3 +190,56 @@ def test_append_rejections_write_nothing():
                            2) == (0, "batch_index")
     rc0 = np.zeros_like(case.page_refcounts)
     assert _reject(case, page_refcounts=rc0)[0] == "not_exclusive"
+
+
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_plain_append_round_trip(layout):
+    """Plain append read back through the (separately pinned) gather: every
+    sequence's rows are exactly the k and v given, and no other slot moves."""
+    lens = [5, 37, 16]
+    case = W.append_case(7, seq_lens=lens, num_qo_heads=8, num_kv_heads=2, layout=layout,
+                         extra_pages=1, spare_pages=3)
+    kv = case.kv
+    reason, kp, vp = R.paged_append(case.k, case.v, case.batch_indices, case.positions,
+                                    kv.k_pool, kv.v_pool, layout, kv.page_indptr,
+                                    kv.page_indices, case.page_refcounts)
+    assert reason is None
+    for b, n in enumerate(lens):
+        s = int(case.qo_indptr[b])
+        assert np.array_equal(A.gather(kp, layout, kv.page_indptr, kv.page_indices, b, n),
+                              bf16.to_f64(case.k[s:s + n]))
+        assert np.array_equal(A.gather(vp, layout, kv.page_indptr, kv.page_indices, b, n),
+                              bf16.to_f64(case.v[s:s + n]))
+    n_rows = sum(lens) * 2 * D                      # elements written per pool
+    assert np.count_nonzero(kp != kv.k_pool) <= n_rows
+    assert np.count_nonzero(vp != kv.v_pool) <= n_rows
+
+
+def test_plain_append_equals_fused_append_at_position_zero():
+    """At position 0 the rotation angle is 0 for every pair (cos 1, sin 0), so
+    the fused RoPE append must store exactly what the plain append stores."""
+    B = 6
+    case = W.append_case(8, seq_lens=[1] * B, num_qo_heads=4, num_kv_heads=2)
+    kv = case.kv
+    assert not case.positions.any()
+    r1, kp1, vp1 = R.paged_append(case.k, case.v, case.batch_indices, case.positions,
+                                  kv.k_pool, kv.v_pool, kv.layout, kv.page_indptr,
+                                  kv.page_indices, case.page_refcounts)
+    r2, _, kp2, vp2 = R.paged_append_rope(case.q, case.k, case.v, case.batch_indices,
+                                          case.positions, kv.k_pool, kv.v_pool, kv.layout,
+                                          kv.page_indptr, kv.page_indices, case.page_refcounts,
+                                          10000.0)
+    assert r1 is None and r2 is None
+    assert np.array_equal(kp1, kp2) and np.array_equal(vp1, vp2)
+
+
+def test_plain_append_rejections_write_nothing():
+    case = W.append_case(9, seq_lens=[20, 9], num_qo_heads=4, num_kv_heads=1)
+    kv = case.kv
+    rc = case.page_refcounts.copy()
+    rc[kv.page_indices[0]] = 3
+    reason, kp, vp = R.paged_append(case.k, case.v, case.batch_indices, case.positions,
+                                    kv.k_pool, kv.v_pool, kv.layout, kv.page_indptr,
+                                    kv.page_indices, rc)
+    assert reason == "not_exclusive"
+    assert np.array_equal(kp, kv.k_pool) and np.array_equal(vp, kv.v_pool)
