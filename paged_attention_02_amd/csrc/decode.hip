@@ -118,24 +118,6 @@ void paged_decode_kernel(DecodeParams p) {
                       (int64_t)(hi - lo) * kPage >= (int64_t)L;
   const bool seq_ok = len_ok && ptr_ok;
 
-  if (p.status != nullptr && part == 0 && kvh == 0 && ht == 0) {
-    int code = 0;
-    if (!len_ok) {
-      code = kStatusSeqLen;
-    } else if (!ptr_ok) {
-      code = kStatusIndptr;
-    } else {
-      const int need = (L + kPage - 1) / kPage;
-      int bad = 0;
-      for (int i = tid; i < need; i += kNW * 64) {
-        const int pid = p.page_indices[lo + i];
-        bad |= (pid < 0 || pid >= p.num_pages);
-      }
-      if (__syncthreads_or(bad)) code = kStatusPageRange;
-    }
-    if (tid == 0) p.status[b] = code;
-  }
-
   const int chunk_tokens = p.chunk_pages * kPage;
   const int t0 = part * chunk_tokens;
   const int t1 = seq_ok ? min(t0 + chunk_tokens, L) : t0;
@@ -350,24 +332,57 @@ void paged_decode_kernel(DecodeParams p) {
       red_o[(wave * kHeadDim + 16 * j + 4 * gq + i) * kHT + col] = acc[j][i] * f;
   __syncthreads();
   const bool split = p.num_partitions > 1;
-  for (int idx = tid; idx < ncol * kHeadDim; idx += kNW * 64) {
-    const int c = idx % ncol;
-    const int dd = idx / ncol;
-    float val = 0.f;
+  {
+    // thread (c, dc): q head c of the tile, dims 8*dc .. 8*dc+7, one 16-byte store
+    const int c = tid >> 4;
+    const int dc = tid & 15;
+    if (c < ncol) {
+      float val[8];
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) val += red_o[(w * kHeadDim + dd) * kHT + c];
-    const float lc = col_l[c];
-    const float lse_val = lc > 0.f ? (col_m[c] + __log2f(lc)) * kLn2 : -INFINITY;
-    const int64_t hrow = (int64_t)b * p.hq + kvh * p.group + ht * kHT + c;
-    if (split) {
-      const int64_t prow = hrow * p.num_partitions + part;
-      p.ws_o[prow * kHeadDim + dd] = val;
-      if (dd == 0) p.ws_lse[prow] = lse_val;
-    } else {
-      p.o[hrow * kHeadDim + dd] = (uint16_t)(pack_bf16x2(val, 0.f) & 0xffffu);
-      if (dd == 0 && p.lse != nullptr) p.lse[hrow] = lse_val;
+      for (int i = 0; i < 8; ++i) {
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) v += red_o[(w * kHeadDim + 8 * dc + i) * kHT + c];
+        val[i] = v;
+      }
+      const float lc = col_l[c];
+      const float lse_val = lc > 0.f ? (col_m[c] + __log2f(lc)) * kLn2 : -INFINITY;
+      const int64_t hrow = (int64_t)b * p.hq + kvh * p.group + ht * kHT + c;
+      if (split) {
+        const int64_t prow = hrow * p.num_partitions + part;
+        float* dst = p.ws_o + prow * kHeadDim + 8 * dc;
+        *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{val[0], val[1], val[2], val[3]};
+        *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{val[4], val[5], val[6], val[7]};
+        if (dc == 0) p.ws_lse[prow] = lse_val;
+      } else {
+        *reinterpret_cast<u32x4_t*>(p.o + hrow * kHeadDim + 8 * dc) =
+            u32x4_t{pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3]),
+                    pack_bf16x2(val[4], val[5]), pack_bf16x2(val[6], val[7])};
+        if (dc == 0 && p.lse != nullptr) p.lse[hrow] = lse_val;
+      }
     }
   }
+
+  // ---- per-sequence status, after the attention so that it does not delay
+  // the start of the K/V stream of the sequence's first work-group
+  if (p.status != nullptr && part == 0 && kvh == 0 && ht == 0) {
+    int code = 0;
+    if (!len_ok) {
+      code = kStatusSeqLen;
+    } else if (!ptr_ok) {
+      code = kStatusIndptr;
+    } else {
+      const int need = (L + kPage - 1) / kPage;
+      int bad = 0;
+      for (int i = tid; i < need; i += kNW * 64) {
+        const int pid = p.page_indices[lo + i];
+        bad |= (pid < 0 || pid >= p.num_pages);
+      }
+      if (__syncthreads_or(bad)) code = kStatusPageRange;
+    }
+    if (tid == 0) p.status[b] = code;
+  }
+
 }
 
 template <int LAYOUT>
