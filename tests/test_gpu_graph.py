@@ -176,7 +176,8 @@ def test_long_paged_prefill_graph_replays_and_rejects_invalid_pages():
     assert torch.equal(outs["g"][0], outs["e"][0])
 
 
-def test_append_graph_replays_equal_eager_and_reject_a_shared_page():
+@pytest.mark.parametrize("plain", [False, True])
+def test_append_graph_replays_equal_eager_and_reject_a_shared_page(plain):
     case = W.append_case(2800, seq_lens=[300, 37, 129], num_qo_heads=32, num_kv_heads=8,
                          extra_pages=1, spare_pages=3)
     kv = case.kv
@@ -193,11 +194,15 @@ def test_append_graph_replays_equal_eager_and_reject_a_shared_page():
 
     def call(which):
         t = state[which]
-        ok(oxa.oxa_paged_append_rope(q_in, t["q"], k_in, v_in, bi, pos, t["kp"], t["vp"], indptr,
-                                     ids, refc, t["st"], layout=kv.layout,
-                                     rope_theta=case.rope_theta, workspace=ws))
+        if plain:   # the plain append (no RoPE, no q)
+            ok(oxa.oxa_paged_append(k_in, v_in, bi, pos, t["kp"], t["vp"], indptr, ids, refc,
+                                    t["st"], layout=kv.layout, workspace=ws))
+        else:
+            ok(oxa.oxa_paged_append_rope(q_in, t["q"], k_in, v_in, bi, pos, t["kp"], t["vp"],
+                                         indptr, ids, refc, t["st"], layout=kv.layout,
+                                         rope_theta=case.rope_theta, workspace=ws))
 
-    note("graph append: capture")
+    note(f"graph append plain={plain}: capture")
     g = capture(lambda: call("g"))
     rng = np.random.default_rng(2900)
     for rep in range(REPLAYS):
@@ -207,7 +212,7 @@ def test_append_graph_replays_equal_eager_and_reject_a_shared_page():
         g.replay()
         call("e")
         torch.cuda.synchronize()
-        for key in ("kp", "vp", "q", "st"):
+        for key in ("kp", "vp", "st") + (() if plain else ("q",)):
             assert torch.equal(state["g"][key], state["e"][key]), f"replay {rep}: {key}"
         assert host(state["g"]["st"]).tolist() == [0, -1]
     # a target page that another sequence shares (refcount 2): the replay
