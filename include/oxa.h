@@ -4,12 +4,15 @@
  * A C ABI over hand-written HIP kernels.  Four operations make up the path:
  *
  *   oxa_paged_append_rope  fused NeoX RoPE on q/k + append of (k, v) into
- *                          exclusively owned KV pages
+ *                          exclusively owned KV pages (oxa_paged_append:
+ *                          the same append without RoPE)
  *   oxa_paged_decode       paged batch decode (MHA / GQA / MQA), optionally
  *                          split-K over explicit KV partitions with an f32
  *                          partial workspace and a log-sum-exp merge
  *   oxa_ragged_prefill     causal (or full) prefill over packed ragged K/V
- *   oxa_paged_prefill      causal (or full) prefill over paged K/V
+ *   oxa_paged_prefill      causal (or full) prefill over paged K/V (both may
+ *                          split a small call's keys over more compute
+ *                          units, given an optional workspace)
  *
  * and two standalone operations: the attention-state merge
  * (oxa_merge_states, oxa_merge_state_pair), which combines the (output, lse)
@@ -60,8 +63,9 @@
  *          ceil(len / 16).  num_page_entries is the length of page_indices.
  * Alignment. Every bf16 tensor and the workspace must be 16-byte aligned.
  * Softmax. sm_scale must be finite and >= 0.  f32 running max / sum /
- *          accumulator; outputs rounded to bf16 (nearest-even).  lse (optional, may be NULL) is the natural-log
- *          log-sum-exp of the scaled scores of each (query row, q head).
+ *          accumulator; outputs rounded to bf16 (nearest-even).  lse
+ *          (optional, may be NULL) is the natural-log log-sum-exp of the
+ *          scaled scores of each (query row, q head).
  */
 #ifndef OXA_H
 #define OXA_H
