@@ -103,6 +103,29 @@ def test_paged_prefill_matches_oracle_and_ragged_bits(layout):
     assert np.array_equal(rag["o"], got["o"]), "paged and ragged paths disagree on identical data"
 
 
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_paged_prefill_non_causal_more_queries_than_keys(layout):
+    """Full (non-causal) attention allows qo_len > kv_len: 100 queries over 40
+    paged keys, 7 over 300, 65 over 1."""
+    qo, kv = [100, 7, 65], [40, 300, 1]
+    hq, hkv = 16, 4
+    case = W.ragged_case(43, qo_lens=qo, kv_lens=kv, num_qo_heads=hq, num_kv_heads=hkv,
+                         causal=False)
+    ks = [case.k[case.kv_indptr[b]:case.kv_indptr[b + 1]] for b in range(3)]
+    vs = [case.v[case.kv_indptr[b]:case.kv_indptr[b + 1]] for b in range(3)]
+    npages = sum(-(-n // 16) for n in kv) + 3
+    kp, indptr, ids = scatter_pages(ks, npages, layout, np.random.default_rng(3))
+    vp, _, _ = scatter_pages(vs, npages, layout, np.random.default_rng(3))
+    note(f"paged prefill non-causal {layout}")
+    got = run_paged(case.q, case.qo_indptr, kp, vp, layout, indptr, ids, kv, hkv, case.sm_scale,
+                    causal=False)
+    o, lse = A.paged_prefill(case.q, case.qo_indptr, kp, vp, layout, indptr, ids,
+                             np.array(kv, np.int32), case.sm_scale, False)
+    assert (got["status"] == 0).all()
+    assert_attention_close(got["o"], o, f"paged non-causal {layout}")
+    assert_lse_close(got["lse"], lse)
+
+
 def test_paged_prefill_status():
     lens = [40, 40, 40]
     case = W.ragged_case(42, qo_lens=lens, num_qo_heads=4, num_kv_heads=1)
