@@ -301,14 +301,14 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
         if (lane == 0) red[wave] = __builtin_popcountll(mask);
         __syncthreads();
-        int before = 0, chunk = 0;
+        int before = 0, here = 0;  // qualifying sequences before this wave / in this pass
         for (int w = 0; w < kNW; ++w) {
           before += w < wave ? red[w] : 0;
-          chunk += red[w];
+          here += red[w];
         }
         if (has && seen + before + pos == rank) sel_b = bb;
         __syncthreads();
-        seen += chunk;
+        seen += here;
         if (seen > rank) break;
       }
       __syncthreads();
