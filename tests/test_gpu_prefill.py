@@ -126,6 +126,48 @@ def test_paged_prefill_non_causal_more_queries_than_keys(layout):
     assert_lse_close(got["lse"], lse)
 
 
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+@pytest.mark.parametrize("split", [False, True])
+def test_paged_prefill_across_page_id_windows(layout, split):
+    """A sequence of 40000 keys lists 2500 pages, more than the 2048-page window
+    of page ids the prefill kernel stages at a time: 64 queries at its end and
+    a short second sequence, unsplit and split into 8 key chunks (with the
+    workspace), the last of which starts in the second window."""
+    qo, kv = [64, 5], [40000, 40]
+    hq, hkv = 8, 2
+    case = W.ragged_case(44, qo_lens=qo, kv_lens=kv, num_qo_heads=hq, num_kv_heads=hkv)
+    ks = [case.k[case.kv_indptr[b]:case.kv_indptr[b + 1]] for b in range(2)]
+    vs = [case.v[case.kv_indptr[b]:case.kv_indptr[b + 1]] for b in range(2)]
+    npages = sum(-(-n // 16) for n in kv) + 5
+    kp, indptr, ids = scatter_pages(ks, npages, layout, np.random.default_rng(4))
+    vp, _, _ = scatter_pages(vs, npages, layout, np.random.default_rng(4))
+    assert indptr[1] > 2048
+    ensure_built()
+    q = dev(case.q)
+    o = torch.zeros_like(q)
+    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device="cuda")
+    status = torch.full((2,), -1, dtype=torch.int32, device="cuda")
+    ws = None
+    if split:
+        nb = oxa.oxa_paged_prefill_workspace_bytes(2, q.shape[0], hq)
+        assert nb > 0
+        ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda")
+    note(f"paged prefill across page-id windows {layout} split={split}")
+    rc = oxa.oxa_paged_prefill(q, dev(case.qo_indptr), dev(kp), dev(vp), dev(indptr), dev(ids),
+                               dev(np.array(kv, np.int32)), o, max_qo_len=64, max_seq_len=40000,
+                               sm_scale=case.sm_scale, layout=layout, num_kv_heads=hkv,
+                               causal=True, lse=lse, status=status, workspace=ws)
+    assert rc == oxa.OXA_OK, oxa.status_string(rc)
+    torch.cuda.synchronize()
+    assert host(status).tolist() == [0, 0]
+    if split:
+        assert (ws != 0xFF).any(), "the call did not split"
+    o_ref, lse_ref = A.paged_prefill(case.q, case.qo_indptr, kp, vp, layout, indptr, ids,
+                                     np.array(kv, np.int32), case.sm_scale, True)
+    assert_attention_close(host_bits(o), o_ref, f"windows {layout} split={split}")
+    assert_lse_close(host(lse), lse_ref)
+
+
 def test_paged_prefill_status():
     lens = [40, 40, 40]
     case = W.ragged_case(42, qo_lens=lens, num_qo_heads=4, num_kv_heads=1)
