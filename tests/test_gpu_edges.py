@@ -9,6 +9,8 @@
   sequence of an item in several 512-sequence chunks of the batch;
 * paged decode with the largest number of explicit partitions (1024), most
   of them empty;
+* ragged prefill at the schedule's level limit: 256 q heads on one kv head
+  (one-row query tiles) and a 4096-row sequence, 4096 tile levels;
 * paged decode at the largest batch (65535 sequences of one token): each
   output equals the V row of its only key exactly (in value: -0 comes out
   as +0, since the accumulator starts at +0).
@@ -136,3 +138,22 @@ def test_decode_at_the_largest_batch():
     got = bf16.to_f64(host_bits(o))
     want = bf16.to_f64(v_pool[perm, 0])                         # [B, 1, 128]
     assert np.array_equal(got[:, 0], want[:, 0]) and np.array_equal(got[:, 1], want[:, 0])
+
+
+def test_prefill_schedule_at_its_level_limit():
+    """256 q heads on one kv head make a query tile one row (BM = 1), so a
+    4096-row sequence gives the 4096 tile levels the schedule can order (the
+    largest max_qo_len the ABI accepts for this grouping).  Sampled rows
+    against the oracle."""
+    case = W.ragged_case(4700, qo_lens=[4096, 7], kv_lens=[4096, 300], num_qo_heads=256,
+                         num_kv_heads=1)
+    note("ragged prefill with 4096 tile levels")
+    o, lse, status = ragged(case)
+    assert (status == 0).all()
+    rng = np.random.default_rng(4701)
+    rows = np.unique(np.concatenate([[0, 1, 2, 4094, 4095, 4096, 4102],
+                                     rng.integers(0, 4103, size=40)]))
+    o_ref, lse_ref = A.ragged_prefill(case.q, case.k, case.v, case.qo_indptr, case.kv_indptr,
+                                      case.sm_scale, True, rows=rows)
+    assert_attention_close(o[rows], o_ref[rows], "4096 levels")
+    assert_lse_close(lse[rows], lse_ref[rows])

@@ -79,6 +79,7 @@ def call_ragged(**over):
     (dict(max_qo=0), oxa.OXA_ERR_SHAPE),
     (dict(scale=float("-inf")), oxa.OXA_ERR_SHAPE),
     (dict(max_qo=1 << 30), oxa.OXA_ERR_SHAPE),       # more query tiles than the grid allows
+    (dict(hq=256, hkv=1, max_qo=4097), oxa.OXA_ERR_SHAPE),  # one-row tiles: at most 4096 levels
     (dict(v=addr(2) + 4), oxa.OXA_ERR_ALIGN),
     (dict(o=addr(1) + 256), oxa.OXA_ERR_ALIAS),      # o overlaps k
     (dict(status=addr(4)), oxa.OXA_ERR_ALIAS),       # status over kv_indptr
