@@ -90,6 +90,23 @@ def test_grouped_decode_mixed_lengths(hq, hkv, P):
 
 
 @pytest.mark.parametrize("layout", ["NHD", "HND"])
+@pytest.mark.parametrize("P", [1, 2])
+def test_decode_several_head_tiles_per_kv_head(layout, P):
+    """24 q heads per kv head: two work-groups (16 + 8 heads) read the same K/V
+    rows, the kernel form with plain (not non-temporal) loads, in both layouts."""
+    lens = [5, 160, 1000, 47]
+    case = W.decode_case(90 + P, batch=len(lens), num_qo_heads=48, num_kv_heads=2, seq_lens=lens,
+                         num_pages=sum(-(-n // 16) for n in lens) + 4, layout=layout,
+                         num_partitions=P, poison=True)
+    note(f"decode 24 q heads per kv head {layout} P={P}")
+    got = run_decode(case)
+    o, lse = oracle_decode(case)
+    assert (got["status"] == 0).all()
+    assert_attention_close(got["o"], o, f"24 heads per kv head {layout} P={P}")
+    assert_lse_close(got["lse"], lse)
+
+
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
 def test_batch_gqa4_decode_full_size(layout):
     # the batch-32 GQA4 workload at full size: every output checked
     case = W.decode_gqa4_batch(poison=True, layout=layout)
