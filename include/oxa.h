@@ -48,6 +48,12 @@
  *          read or write outside the regions the arguments describe, whatever
  *          the metadata holds.  Rows of a sequence whose status is non-zero
  *          are unspecified.
+ *          OXA_ERR_LAUNCH is the one exception to "nothing enqueued": an
+ *          operation of two kernels (append check + writer, split-K decode +
+ *          merge, key-split prefill + merge) whose second launch is refused
+ *          leaves the first one enqueued; its outputs and status are then
+ *          unspecified.  Host validation rules out every launch shape the
+ *          runtime could refuse, so this code means a failing runtime.
  * Domain.  head_dim must be 128 and page_size 16 (OXA_ERR_UNSUPPORTED else).
  *          Head grouping: num_qo_heads % num_kv_heads == 0; q head h reads
  *          kv head h / (num_qo_heads / num_kv_heads).
@@ -62,7 +68,9 @@
  *          than its length needs; attention reads only the first
  *          ceil(len / 16).  num_page_entries is the length of page_indices.
  * Alignment. Every bf16 tensor and the workspace must be 16-byte aligned.
- * Softmax. sm_scale must be finite and >= 0.  f32 running max / sum /
+ * Softmax. sm_scale must be finite and >= 0 (0 weighs every visible key
+ *          alike: the output is the mean of their V rows and lse = ln(count);
+ *          masked keys and tail slots still weigh nothing).  f32 running max / sum /
  *          accumulator; outputs rounded to bf16 (nearest-even).  lse
  *          (optional, may be NULL) is the natural-log log-sum-exp of the
  *          scaled scores of each (query row, q head).
@@ -96,7 +104,7 @@ typedef enum {
   OXA_ERR_ALIGN = 4,         /* a bf16 tensor or the workspace is not 16-byte aligned */
   OXA_ERR_ALIAS = 5,         /* an output region overlaps an input or another output */
   OXA_ERR_WORKSPACE = 6,     /* workspace NULL or smaller than the size query returns */
-  OXA_ERR_LAUNCH = 7,        /* the HIP runtime refused a kernel launch */
+  OXA_ERR_LAUNCH = 7,        /* the HIP runtime refused a kernel launch (see Errors) */
   /* written to status[] on the stream by the kernels */
   OXA_DEV_PAGE_RANGE = 16,   /* a needed page id is outside [0, num_pages) */
   OXA_DEV_INDPTR = 17,       /* indptr out of order / beyond its array, or too few pages */

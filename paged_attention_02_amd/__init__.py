@@ -158,6 +158,28 @@ def _shape(t, shape, name):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def _pools(k_pages, v_pages, lay, hkv=None):
+    """Check a K/V pool pair: [pages, 16, Hkv, 128] (NHD) or [pages, Hkv, 16, 128]
+    (HND), V shaped as K; returns Hkv."""
+    if k_pages.dim() != 4:
+        raise ValueError(f"k_pages must have 4 dimensions, got shape {tuple(k_pages.shape)}")
+    heads = k_pages.shape[2] if lay == 0 else k_pages.shape[1]
+    slots = k_pages.shape[1] if lay == 0 else k_pages.shape[2]
+    if slots != PAGE_SIZE:
+        raise ValueError(f"k_pages holds {slots} slots per page, expected {PAGE_SIZE}")
+    if hkv is not None and heads != hkv:
+        raise ValueError(f"k_pages holds {heads} kv heads, expected {hkv}")
+    _shape(v_pages, k_pages.shape, "v_pages")
+    return heads
+
+
+def _no_alloc_under_capture(what):
+    import torch
+    if torch.cuda.is_current_stream_capturing():
+        raise RuntimeError(f"{what}: pass `workspace` when capturing a graph "
+                           "(the binding would otherwise allocate one inside the capture)")
+
+
 def _stream(stream) -> int:
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -185,11 +207,23 @@ def oxa_paged_append_rope(q_in, q_out, k_in, v_in, batch_indices, positions, k_p
     bytes is allocated on k_in's device.
     """
     lay = _layout(layout)
-    hkv = k_in.shape[1]
+    nnz, hkv = k_in.shape[0], k_in.shape[1]
     num_pages = k_pages.shape[0]
     hq = q_in.shape[1] if q_in is not None else 0
+    if q_in is not None:
+        _shape(q_in, (nnz, hq, k_in.shape[2]), "q_in")
+        _shape(q_out, q_in.shape, "q_out")
+    elif q_out is not None:
+        raise ValueError("q_out given without q_in")
+    _shape(v_in, k_in.shape, "v_in")
+    _shape(batch_indices, (nnz,), "batch_indices")
+    _shape(positions, (nnz,), "positions")
+    _pools(k_pages, v_pages, lay, hkv)
+    _shape(page_refcounts, (num_pages,), "page_refcounts")
+    _shape(status, (2,), "status")
     if workspace is None:
         import torch
+        _no_alloc_under_capture("oxa_paged_append_rope")
         nbytes = oxa_paged_append_rope_workspace_bytes(k_in.shape[0])
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=k_in.device)
     ws_bytes = workspace.numel() * workspace.element_size()
@@ -213,8 +247,16 @@ def oxa_paged_append(k_in, v_in, batch_indices, positions, k_pages, v_pages, pag
     """Plain append of (k, v) rows into exclusive pages, no rotation; arguments
     as for oxa_paged_append_rope without q and rope_theta."""
     lay = _layout(layout)
+    nnz = k_in.shape[0]
+    _shape(v_in, k_in.shape, "v_in")
+    _shape(batch_indices, (nnz,), "batch_indices")
+    _shape(positions, (nnz,), "positions")
+    _pools(k_pages, v_pages, lay, k_in.shape[1])
+    _shape(page_refcounts, (k_pages.shape[0],), "page_refcounts")
+    _shape(status, (2,), "status")
     if workspace is None:
         import torch
+        _no_alloc_under_capture("oxa_paged_append")
         nbytes = oxa_paged_append_workspace_bytes(k_in.shape[0])
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=k_in.device)
     ws_bytes = workspace.numel() * workspace.element_size()
@@ -237,8 +279,13 @@ def oxa_paged_decode(q, k_pages, v_pages, page_indptr, page_indices, seq_lens, o
                      workspace=None, lse=None, status=None, stream=None) -> int:
     """Paged batch decode: q/o [B, Hq, 128]; lse [B, Hq] f32; status [B] int32."""
     lay = _layout(layout)
-    if num_kv_heads is None:
-        num_kv_heads = k_pages.shape[2] if lay == 0 else k_pages.shape[1]
+    num_kv_heads = _pools(k_pages, v_pages, lay, num_kv_heads)
+    B, hq = q.shape[0], q.shape[1]
+    _shape(o, q.shape, "o")
+    _shape(lse, (B, hq), "lse")
+    _shape(status, (B,), "status")
+    _shape(seq_lens, (B,), "seq_lens")
+    _shape(page_indptr, (B + 1,), "page_indptr")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return lib().oxa_paged_decode(
         _stream(stream), _bf16(q, "q"), q.shape[0], q.shape[1], num_kv_heads, q.shape[2],
@@ -266,6 +313,12 @@ def oxa_ragged_prefill(q, k, v, qo_indptr, kv_indptr, o, *, max_qo_len, max_kv_l
     """Ragged prefill: q/o [nnz_qo, Hq, 128]; k/v [nnz_kv, Hkv, 128].  With a
     ``workspace`` of oxa_ragged_prefill_workspace_bytes(...) bytes, small calls
     split their keys over more CUs."""
+    B = qo_indptr.shape[0] - 1
+    _shape(kv_indptr, qo_indptr.shape, "kv_indptr")
+    _shape(v, k.shape, "v")
+    _shape(o, q.shape, "o")
+    _shape(lse, (q.shape[0], q.shape[1]), "lse")
+    _shape(status, (B,), "status")
     return lib().oxa_ragged_prefill(
         _stream(stream), _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"),
         _i32(qo_indptr, "qo_indptr"), _i32(kv_indptr, "kv_indptr"), qo_indptr.shape[0] - 1,
@@ -281,8 +334,13 @@ def oxa_paged_prefill(q, qo_indptr, k_pages, v_pages, page_indptr, page_indices,
     """Paged prefill: q/o [nnz_qo, Hq, 128] over the paged K/V of each sequence
     (``workspace`` as for oxa_ragged_prefill)."""
     lay = _layout(layout)
-    if num_kv_heads is None:
-        num_kv_heads = k_pages.shape[2] if lay == 0 else k_pages.shape[1]
+    num_kv_heads = _pools(k_pages, v_pages, lay, num_kv_heads)
+    B = qo_indptr.shape[0] - 1
+    _shape(page_indptr, (B + 1,), "page_indptr")
+    _shape(seq_lens, (B,), "seq_lens")
+    _shape(o, q.shape, "o")
+    _shape(lse, (q.shape[0], q.shape[1]), "lse")
+    _shape(status, (B,), "status")
     return lib().oxa_paged_prefill(
         _stream(stream), _bf16(q, "q"), _i32(qo_indptr, "qo_indptr"), _bf16(k_pages, "k_pages"),
         _bf16(v_pages, "v_pages"), k_pages.shape[0], PAGE_SIZE, lay,

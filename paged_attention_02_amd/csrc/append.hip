@@ -278,8 +278,7 @@ hipError_t launch_paged_append_rope(const AppendLaunch& a, hipStream_t stream) {
   for (int i = 0; i < 64; ++i) p.inv_freq[i] = a.inv_freq[i];
   p.check = a.check;
   p.check_groups = append_check_groups(a.nnz);
-  hipLaunchKernelGGL(append_check_kernel, dim3(p.check_groups), dim3(256), 0, stream, p);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_kernel(append_check_kernel, dim3(p.check_groups), dim3(256), 0, stream, p);
   if (e != hipSuccess) return e;
   // the writer also reports the status, so it runs even for nnz == 0
   int blocks = (a.nnz + 3) / 4;
@@ -289,8 +288,7 @@ hipError_t launch_paged_append_rope(const AppendLaunch& a, hipStream_t stream) {
                                                            : append_rope_kernel<1, true>)
                                         : (a.layout == 0 ? append_rope_kernel<0, false>
                                                          : append_rope_kernel<1, false>);
-  hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), 0, stream, p);
-  return hipGetLastError();
+  return launch_kernel(kernel, dim3(blocks), dim3(256), 0, stream, p);
 }
 
 }  // namespace oxa

@@ -253,7 +253,10 @@ void paged_decode_kernel(DecodeParams p) {
             mraw = fmaxf(mraw, s[mb][i]);
           }
       }
-      const float mblk = pair_max32(xor16_max(mraw)) * p.scale_log2;
+      // a block with no visible key keeps max -inf (also for a zero scale,
+      // where -inf * 0 would be NaN)
+      const float mred = pair_max32(xor16_max(mraw));
+      const float mblk = mred == -INFINITY ? -INFINITY : mred * p.scale_log2;
       // Lazy rescaling: exponentials are taken against a reference max that
       // only moves when a score exceeds it by more than 2^8, so probabilities
       // stay <= 256 and the accumulator is rescaled rarely.  The result is
@@ -272,6 +275,12 @@ void paged_decode_kernel(DecodeParams p) {
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) pv[4 * mb + i] = fast_exp2(fmaf(s[mb][i], p.scale_log2, -muse));
+      if (!full) {
+        // masked keys weigh exactly 0: with a zero scale fmaf(-inf, 0, x) is
+        // NaN, so the weight is selected, not computed
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pv[i] = s[i >> 2][i & 3] == -INFINITY ? 0.f : pv[i];
+      }
       lsum += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
       // P^T B operand: k slot j of lane l is token (j < 4 ? 4gq + j : 16 + 4gq + j - 4)
       const u32x4_t pf = u32x4_t{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
@@ -402,8 +411,7 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
   const int64_t groups = ((int64_t)(p.num_items + 7) / 8) * 8 * p.head_tiles;
   void (*kernel)(DecodeParams) =
       p.head_tiles == 1 ? paged_decode_kernel<LAYOUT, true> : paged_decode_kernel<LAYOUT, false>;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)groups), dim3(kNW * 64), lds, stream, p);
-  return hipGetLastError();
+  return launch_kernel(kernel, dim3((unsigned)groups), dim3(kNW * 64), lds, stream, p);
 }
 
 }  // namespace

@@ -31,6 +31,15 @@ typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
+// Launch a kernel whose one argument is a parameter struct; the launch's own
+// status is returned (not a sticky error left by an earlier, unrelated call).
+template <typename P>
+inline hipError_t launch_kernel(void (*kernel)(P), dim3 grid, dim3 block, size_t lds,
+                                hipStream_t stream, const P& params) {
+  void* args[] = {const_cast<P*>(&params)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, lds, stream);
+}
+
 constexpr int kPage = 16;
 constexpr int kHeadDim = 128;
 constexpr float kLog2e = 1.4426950408889634f;

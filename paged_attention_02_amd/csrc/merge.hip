@@ -137,13 +137,9 @@ template <bool IN_F32, bool OUT_F32>
 hipError_t launch_t(const MergeLaunch& a, hipStream_t stream) {
   constexpr int kUpb = kThreads / (kHeadDim / (16 / (IN_F32 ? 4 : 2)));
   const int64_t groups = (a.units + kUpb - 1) / kUpb;
-  if (a.pair)
-    hipLaunchKernelGGL((merge_states_kernel<IN_F32, OUT_F32, true>), dim3((unsigned)groups),
-                       dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((merge_states_kernel<IN_F32, OUT_F32, false>), dim3((unsigned)groups),
-                       dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  void (*kernel)(MergeLaunch) = a.pair ? merge_states_kernel<IN_F32, OUT_F32, true>
+                                       : merge_states_kernel<IN_F32, OUT_F32, false>;
+  return launch_kernel(kernel, dim3((unsigned)groups), dim3(kThreads), 0, stream, a);
 }
 
 }  // namespace

@@ -455,7 +455,9 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
         }
         // raw-score max (the scale is >= 0, so it commutes with max), then
         // lazy rescaling: the reference max moves only when exceeded by 2^8
-        const float mt = pair_max32(mraw) * p.scale_log2;
+        // (a block with no visible key keeps -inf, also for a zero scale)
+        const float mred = pair_max32(mraw);
+        const float mt = mred == -INFINITY ? -INFINITY : mred * p.scale_log2;
         if (__builtin_amdgcn_ballot_w64(mt > m[cb] + 8.f) != 0) {
           const float mnew = mt > m[cb] + 8.f ? mt : m[cb];
           const float corr = fast_exp2(m[cb] - mnew);  // 0 while m is still -inf
@@ -468,12 +470,26 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
         }
         const float muse = m[cb] == -INFINITY ? 0.f : m[cb];
         float psum = 0.f;
+        if (need_mask) {
+          // masked keys weigh exactly 0: with a zero scale fmaf(-inf, 0, x)
+          // is NaN, so the weight is selected, not computed
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(fmaf(s[cb][r], p.scale_log2, -muse));
-          const float p1 = fast_exp2(fmaf(s[cb][r + 1], p.scale_log2, -muse));
-          psum += p0 + p1;
-          pk[cb][r >> 1] = pack_bf16x2(p0, p1);
+          for (int r = 0; r < 16; r += 2) {
+            float p0 = fast_exp2(fmaf(s[cb][r], p.scale_log2, -muse));
+            float p1 = fast_exp2(fmaf(s[cb][r + 1], p.scale_log2, -muse));
+            p0 = s[cb][r] == -INFINITY ? 0.f : p0;
+            p1 = s[cb][r + 1] == -INFINITY ? 0.f : p1;
+            psum += p0 + p1;
+            pk[cb][r >> 1] = pack_bf16x2(p0, p1);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const float p0 = fast_exp2(fmaf(s[cb][r], p.scale_log2, -muse));
+            const float p1 = fast_exp2(fmaf(s[cb][r + 1], p.scale_log2, -muse));
+            psum += p0 + p1;
+            pk[cb][r >> 1] = pack_bf16x2(p0, p1);
+          }
         }
         lsum[cb] += psum;
       }
@@ -635,8 +651,7 @@ hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream) {
     kernel = split ? prefill_kernel<true, 0, true> : prefill_kernel<true, 0, false>;
   else
     kernel = split ? prefill_kernel<true, 1, true> : prefill_kernel<true, 1, false>;
-  hipLaunchKernelGGL(kernel, grid, block, 0, stream, p);
-  e = hipGetLastError();
+  e = launch_kernel(kernel, grid, block, 0, stream, p);
   if (e != hipSuccess || p.split == 1) return e;
   // merge the chunks: ws [split][nnz_qo][hq][128] f32 -> o [nnz_qo][hq][128] bf16
   MergeLaunch m = {};

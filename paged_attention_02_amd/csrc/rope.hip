@@ -104,8 +104,7 @@ hipError_t launch_rope(const RopeLaunch& a, hipStream_t stream) {
   for (int i = 0; i < 64; ++i) p.inv_freq[i] = a.inv_freq[i];
   int64_t groups = ((int64_t)a.nnz + kWaves - 1) / kWaves;
   if (groups > kMaxGroups) groups = kMaxGroups;
-  hipLaunchKernelGGL(rope_kernel, dim3((unsigned)groups), dim3(kWaves * 64), 0, stream, p);
-  return hipGetLastError();
+  return launch_kernel(rope_kernel, dim3((unsigned)groups), dim3(kWaves * 64), 0, stream, p);
 }
 
 }  // namespace oxa
