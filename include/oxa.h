@@ -35,7 +35,8 @@
  *          CUDA tensor), except where a comment says "host".  The caller owns
  *          all memory.  The library allocates nothing, frees nothing, keeps no
  *          pointer after the call returns and keeps no state between calls
- *          apart from a per-device cache of the compute-unit count.
+ *          apart from a per-device cache of the compute-unit count and, for
+ *          oxa_paged_decode_noalloc only, its static per-GPU scratch array.
  * Stream.  Work is enqueued on `stream` (0 = the null stream) and the call
  *          returns without synchronising.  Buffers must stay valid, and inputs
  *          unmodified, until that work completes.
@@ -86,7 +87,7 @@
 extern "C" {
 #endif
 
-#define OXA_ABI_VERSION 6
+#define OXA_ABI_VERSION 7
 #define OXA_PAGE_SIZE 16
 #define OXA_HEAD_DIM 128
 
@@ -105,6 +106,8 @@ typedef enum {
   OXA_ERR_ALIAS = 5,         /* an output region overlaps an input or another output */
   OXA_ERR_WORKSPACE = 6,     /* workspace NULL or smaller than the size query returns */
   OXA_ERR_LAUNCH = 7,        /* the HIP runtime refused a kernel launch (see Errors) */
+  OXA_ERR_SCRATCH_LIMIT = 8, /* oxa_paged_decode_noalloc: the partial states need more than
+                                OXA_DECODE_SCRATCH_BYTES */
   /* written to status[] on the stream by the kernels */
   OXA_DEV_PAGE_RANGE = 16,   /* a needed page id is outside [0, num_pages) */
   OXA_DEV_INDPTR = 17,       /* indptr out of order / beyond its array, or too few pages */
@@ -240,6 +243,33 @@ oxa_status oxa_paged_decode(
     const int32_t* seq_lens, int32_t max_seq_len,
     float sm_scale, int32_t num_partitions,
     void* workspace, size_t workspace_bytes,
+    uint16_t* o, float* lse, int32_t* status);
+
+/*
+ * Allocation-free paged decode, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): oxa_paged_decode with the same arguments, results and
+ * status, minus the workspace.  The split-K partial states go to a static
+ * scratch array inside the library instead, OXA_DECODE_SCRATCH_BYTES per GPU,
+ * which each GPU the library runs on holds until the process ends.  A call
+ * whose states need more (oxa_paged_decode_workspace_bytes > the limit, i.e.
+ * batch * num_qo_heads * num_partitions > 16256) returns
+ * OXA_ERR_SCRATCH_LIMIT and enqueues nothing.  The call allocates and frees
+ * nothing; its first call on a device resolves that device's scratch address
+ * once.  Every call on one GPU shares that GPU's scratch, so calls that may
+ * overlap in time on one GPU (other streams, other host threads) race and
+ * must be ordered by the caller.  After a split call the scratch holds the
+ * partial states laid out as oxa_paged_decode's workspace.
+ */
+#define OXA_DECODE_SCRATCH_BYTES ((size_t)8 << 20)
+oxa_status oxa_paged_decode_noalloc(
+    hipStream_t stream,
+    const uint16_t* q, int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+    const uint16_t* k_pages, const uint16_t* v_pages, int32_t num_pages, int32_t page_size,
+    int32_t layout,
+    const int32_t* page_indptr, const int32_t* page_indices, int32_t num_page_entries,
+    const int32_t* seq_lens, int32_t max_seq_len,
+    float sm_scale, int32_t num_partitions,
     uint16_t* o, float* lse, int32_t* status);
 
 /* Workspace bytes oxa_paged_decode needs (0 for num_partitions == 1). */

@@ -29,6 +29,8 @@ OXA_ERR_ALIGN = 4
 OXA_ERR_ALIAS = 5
 OXA_ERR_WORKSPACE = 6
 OXA_ERR_LAUNCH = 7
+OXA_ERR_SCRATCH_LIMIT = 8
+OXA_DECODE_SCRATCH_BYTES = 8 << 20
 OXA_DEV_PAGE_RANGE = 16
 OXA_DEV_INDPTR = 17
 OXA_DEV_SEQ_LEN = 18
@@ -60,6 +62,8 @@ SIGNATURES = {
     "oxa_paged_decode": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _P, _P, _I, _P, _I, _F,
                               _I, _P, _Z, _P, _P, _P]),
     "oxa_paged_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
+    "oxa_paged_decode_noalloc": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _P, _P, _I, _P,
+                                      _I, _F, _I, _P, _P, _P]),
     "oxa_ragged_prefill": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                                 _P, _Z, _P, _P, _P]),
     "oxa_ragged_prefill_workspace_bytes": (_Z, [_I, _I, _I, _I]),
@@ -294,6 +298,28 @@ def oxa_paged_decode(q, k_pages, v_pages, page_indptr, page_indices, seq_lens, o
         page_indices.shape[0], _i32(seq_lens, "seq_lens"), int(max_seq_len), float(sm_scale),
         int(num_partitions), _ptr(workspace), ws_bytes, _bf16(o, "o"), _f32(lse, "lse"),
         _i32(status, "status"))
+
+
+def oxa_paged_decode_noalloc(q, k_pages, v_pages, page_indptr, page_indices, seq_lens, o, *,
+                             max_seq_len, sm_scale, layout="NHD", num_kv_heads=None,
+                             num_partitions=1, lse=None, status=None, stream=None) -> int:
+    """oxa_paged_decode without a workspace: the split-K partial states go to
+    the library's static per-GPU scratch (OXA_DECODE_SCRATCH_BYTES), so the
+    call allocates nothing; calls that overlap on one GPU race on it."""
+    lay = _layout(layout)
+    num_kv_heads = _pools(k_pages, v_pages, lay, num_kv_heads)
+    B, hq = q.shape[0], q.shape[1]
+    _shape(o, q.shape, "o")
+    _shape(lse, (B, hq), "lse")
+    _shape(status, (B,), "status")
+    _shape(seq_lens, (B,), "seq_lens")
+    _shape(page_indptr, (B + 1,), "page_indptr")
+    return lib().oxa_paged_decode_noalloc(
+        _stream(stream), _bf16(q, "q"), B, hq, num_kv_heads, q.shape[2],
+        _bf16(k_pages, "k_pages"), _bf16(v_pages, "v_pages"), k_pages.shape[0], PAGE_SIZE, lay,
+        _i32(page_indptr, "page_indptr"), _i32(page_indices, "page_indices"),
+        page_indices.shape[0], _i32(seq_lens, "seq_lens"), int(max_seq_len), float(sm_scale),
+        int(num_partitions), _bf16(o, "o"), _f32(lse, "lse"), _i32(status, "status"))
 
 
 def oxa_ragged_prefill_workspace_bytes(batch, nnz_qo, num_qo_heads, head_dim=HEAD_DIM) -> int:

@@ -26,6 +26,8 @@
 // reduction plus two lane exchanges, and the probabilities already form the
 // B operand of O^T = V^T P^T (8 more MFMAs, V^T through the LDS transpose
 // read).
+#include <atomic>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -415,6 +417,34 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Scratch of the allocation-free decode entry point: the split-K partial
+// states (o_part, then lse_part) of one call live here instead of in a
+// caller workspace.  Each GPU holds its own copy for the life of the process;
+// every call on that GPU reuses it (a call writes every partial state it
+// later reads, so nothing needs clearing), and calls that overlap on one GPU
+// race on it.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch_address(void** ptr) {
+  // The array's name is a host-side stand-in; its device address is resolved
+  // once per device, with that device current, and kept.
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 hipError_t launch_paged_decode(const DecodeLaunch& a, hipStream_t stream) {
   DecodeParams p;

@@ -23,6 +23,10 @@ struct DecodeLaunch {
   float sm_scale;
 };
 hipError_t launch_paged_decode(const DecodeLaunch& a, hipStream_t stream);
+// Bytes of the per-device static scratch behind the allocation-free decode,
+// and its device address on the current device (resolved once per device).
+constexpr size_t kDecodeScratchBytes = (size_t)8 << 20;
+hipError_t decode_scratch_address(void** ptr);
 
 struct AppendLaunch {
   const uint16_t* q_in;

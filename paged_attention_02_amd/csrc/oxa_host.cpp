@@ -44,6 +44,8 @@ bool any_alias(const Region* outs, int nout, const Region* ins, int nin) {
 }
 
 constexpr uint64_t kRowBytes = OXA_HEAD_DIM * 2;  // one bf16 head row
+static_assert(OXA_DECODE_SCRATCH_BYTES == oxa::kDecodeScratchBytes,
+              "the header states the static decode scratch size");
 constexpr int kMaxGridYZ = 65535;
 constexpr uint64_t kMaxPrefillTiles = 4096;
 
@@ -277,6 +279,7 @@ const char* oxa_status_string(int32_t code) {
     case OXA_ERR_ALIAS: return "OXA_ERR_ALIAS";
     case OXA_ERR_WORKSPACE: return "OXA_ERR_WORKSPACE";
     case OXA_ERR_LAUNCH: return "OXA_ERR_LAUNCH";
+    case OXA_ERR_SCRATCH_LIMIT: return "OXA_ERR_SCRATCH_LIMIT";
     case OXA_DEV_PAGE_RANGE: return "OXA_DEV_PAGE_RANGE";
     case OXA_DEV_INDPTR: return "OXA_DEV_INDPTR";
     case OXA_DEV_SEQ_LEN: return "OXA_DEV_SEQ_LEN";
@@ -338,14 +341,20 @@ size_t oxa_paged_decode_workspace_bytes(int32_t batch, int32_t num_qo_heads, int
   return (size_t)(rows * OXA_HEAD_DIM * 4 + rows * 4);
 }
 
-oxa_status oxa_paged_decode(hipStream_t stream, const uint16_t* q, int32_t batch,
-                            int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
-                            const uint16_t* k_pages, const uint16_t* v_pages, int32_t num_pages,
-                            int32_t page_size, int32_t layout, const int32_t* page_indptr,
-                            const int32_t* page_indices, int32_t num_page_entries,
-                            const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
-                            int32_t num_partitions, void* workspace, size_t workspace_bytes,
-                            uint16_t* o, float* lse, int32_t* status) {
+}  // extern "C"
+
+namespace {
+
+// Both decode entry points.  With `use_scratch` the partial states of a split
+// call go to the library's per-device static scratch instead of `workspace`.
+oxa_status paged_decode_impl(hipStream_t stream, const uint16_t* q, int32_t batch,
+                             int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                             const uint16_t* k_pages, const uint16_t* v_pages, int32_t num_pages,
+                             int32_t page_size, int32_t layout, const int32_t* page_indptr,
+                             const int32_t* page_indices, int32_t num_page_entries,
+                             const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                             int32_t num_partitions, void* workspace, size_t workspace_bytes,
+                             bool use_scratch, uint16_t* o, float* lse, int32_t* status) {
   if (!q || !k_pages || !v_pages || !page_indptr || !page_indices || !seq_lens || !o)
     return OXA_ERR_NULL;
   if (oxa_status s = check_heads(num_qo_heads, num_kv_heads, head_dim)) return s;
@@ -363,7 +372,11 @@ oxa_status oxa_paged_decode(hipStream_t stream, const uint16_t* q, int32_t batch
     return OXA_ERR_ALIGN;
   const size_t need = oxa_paged_decode_workspace_bytes(batch, num_qo_heads, head_dim,
                                                        num_partitions);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return OXA_ERR_WORKSPACE;
+  if (use_scratch) {
+    if (need > oxa::kDecodeScratchBytes) return OXA_ERR_SCRATCH_LIMIT;
+  } else if (need > 0 && (workspace == nullptr || workspace_bytes < need)) {
+    return OXA_ERR_WORKSPACE;
+  }
 
   const uint64_t B = (uint64_t)batch;
   const uint64_t pool = (uint64_t)num_pages * OXA_PAGE_SIZE * (uint64_t)num_kv_heads * kRowBytes;
@@ -376,8 +389,14 @@ oxa_status oxa_paged_decode(hipStream_t stream, const uint16_t* q, int32_t batch
   const Region outs[] = {{o, B * num_qo_heads * kRowBytes},
                          {lse, lse ? B * num_qo_heads * 4 : 0},
                          {status, status ? B * 4 : 0},
-                         {workspace, need}};
+                         {use_scratch ? nullptr : workspace, need}};
   if (any_alias(outs, 4, ins, 6)) return OXA_ERR_ALIAS;
+  if (use_scratch && need > 0) {
+    // the library's own array: it overlaps nothing the caller owns
+    void* p = nullptr;
+    if (oxa::decode_scratch_address(&p) != hipSuccess) return OXA_ERR_LAUNCH;
+    workspace = p;
+  }
 
   oxa::DecodeLaunch a;
   a.q = q;
@@ -404,6 +423,38 @@ oxa_status oxa_paged_decode(hipStream_t stream, const uint16_t* q, int32_t batch
   a.chunk_pages = (max_pages + num_partitions - 1) / num_partitions;
   a.sm_scale = sm_scale;
   return launch_status(oxa::launch_paged_decode(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+oxa_status oxa_paged_decode(hipStream_t stream, const uint16_t* q, int32_t batch,
+                            int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                            const uint16_t* k_pages, const uint16_t* v_pages, int32_t num_pages,
+                            int32_t page_size, int32_t layout, const int32_t* page_indptr,
+                            const int32_t* page_indices, int32_t num_page_entries,
+                            const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                            int32_t num_partitions, void* workspace, size_t workspace_bytes,
+                            uint16_t* o, float* lse, int32_t* status) {
+  return paged_decode_impl(stream, q, batch, num_qo_heads, num_kv_heads, head_dim, k_pages,
+                           v_pages, num_pages, page_size, layout, page_indptr, page_indices,
+                           num_page_entries, seq_lens, max_seq_len, sm_scale, num_partitions,
+                           workspace, workspace_bytes, false, o, lse, status);
+}
+
+oxa_status oxa_paged_decode_noalloc(hipStream_t stream, const uint16_t* q, int32_t batch,
+                                    int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    const uint16_t* k_pages, const uint16_t* v_pages,
+                                    int32_t num_pages, int32_t page_size, int32_t layout,
+                                    const int32_t* page_indptr, const int32_t* page_indices,
+                                    int32_t num_page_entries, const int32_t* seq_lens,
+                                    int32_t max_seq_len, float sm_scale, int32_t num_partitions,
+                                    uint16_t* o, float* lse, int32_t* status) {
+  return paged_decode_impl(stream, q, batch, num_qo_heads, num_kv_heads, head_dim, k_pages,
+                           v_pages, num_pages, page_size, layout, page_indptr, page_indices,
+                           num_page_entries, seq_lens, max_seq_len, sm_scale, num_partitions,
+                           nullptr, 0, true, o, lse, status);
 }
 
 // ---------------------------------------------------------------- prefill

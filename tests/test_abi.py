@@ -29,9 +29,10 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     lib = ensure_built()
-    assert lib.oxa_abi_version() == 6
+    assert lib.oxa_abi_version() == 7
     assert oxa.status_string(0) == "OXA_OK"
     assert oxa.status_string(20) == "OXA_DEV_NOT_EXCLUSIVE"
+    assert oxa.status_string(8) == "OXA_ERR_SCRATCH_LIMIT"
     assert oxa.status_string(999) == "unknown"
 
 

@@ -63,6 +63,33 @@ def test_decode_rejections(over, code):
     assert call_decode(**over) == code
 
 
+def call_decode_noalloc(**over):
+    args = decode_args(**over)
+    del args[18:20]  # the allocation-free form takes no workspace arguments
+    return ensure_built().oxa_paged_decode_noalloc(*args)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), oxa.OXA_ERR_NULL),
+    (dict(head_dim=64), oxa.OXA_ERR_UNSUPPORTED),
+    (dict(P=0), oxa.OXA_ERR_SHAPE),
+    (dict(scale=-0.5), oxa.OXA_ERR_SHAPE),
+    (dict(q=addr(0) + 8), oxa.OXA_ERR_ALIGN),
+    (dict(o=addr(0) + 512), oxa.OXA_ERR_ALIAS),
+    # partial states of 128 x 8 x 16 (row, partition) pairs: 8,454,144 bytes > 8 MiB
+    (dict(batch=128, hq=8, P=16), oxa.OXA_ERR_SCRATCH_LIMIT),
+    (dict(batch=16, hq=8, P=128), oxa.OXA_ERR_SCRATCH_LIMIT),
+])
+def test_decode_noalloc_rejections(over, code):
+    assert call_decode_noalloc(**over) == code
+
+
+def test_decode_noalloc_limit_matches_the_workspace_query():
+    limit = oxa.OXA_DECODE_SCRATCH_BYTES
+    assert oxa.oxa_paged_decode_workspace_bytes(127, 8, 16) <= limit   # 16256 states fit
+    assert oxa.oxa_paged_decode_workspace_bytes(128, 8, 16) > limit
+
+
 def call_ragged(**over):
     args = dict(stream=None, q=addr(0), k=addr(1), v=addr(2), qo=addr(3), kv=addr(4), batch=2,
                 nnz_qo=100, nnz_kv=100, hq=8, hkv=2, head_dim=128, max_qo=64, max_kv=64,
