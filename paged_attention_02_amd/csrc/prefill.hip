@@ -35,11 +35,13 @@ constexpr int kStatusCausal = 19;
 
 constexpr int kBN = 64;              // keys per tile
 constexpr int kNW = 8;               // waves per work-group
-constexpr int kCB = 1;               // 32-column blocks per wave
 constexpr int kLoadIters = kBN * 16 / (kNW * 64);  // 16-byte K (and V) loads per thread per tile
-constexpr int kCols = kNW * kCB * 32;  // (row, head) columns per work-group
+constexpr int kCols = kNW * 32;       // (row, head) columns per work-group
 constexpr int kTileBytes = kBN * 256;  // one K (or V) tile: 64 rows of 256 bytes, swizzled
 constexpr int kMaxLevels = 4096;       // query tiles per sequence the schedule can order
+
+template <int N>
+struct BufTag { static constexpr int value = N; };
 
 struct PrefillParams {
   const uint16_t* q;
@@ -325,40 +327,50 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
   const int kt0 = (int)((int64_t)chunk * ntiles / split);
   const int kt1 = (int)((int64_t)(chunk + 1) * ntiles / split);
 
-  // this lane's columns: (row, head) pairs wave*32*kCB + cb*32 + col
-  bool col_ok[kCB];
-  int qrow[kCB], head[kCB], row_lim[kCB];
-  u32x4_t qf[kCB][8];
+  // this lane's column: (row, head) pair wave*32 + col
+  const int pair = wave * 32 + col;
+  const int prow = pair / p.gwg;
+  const int head_in_group = ht * p.gwg + (pair - prow * p.gwg);
+  const bool col_ok = prow < rows_here && pair < p.bm * p.gwg && head_in_group < p.group;
+  const int qrow = r0 + prow;
+  const int head = kvh * p.group + head_in_group;
+  const int row_lim = qrow + offset;  // last visible key (causal)
+  u32x4_t qf[8];
+  if (col_ok) {
+    const uint16_t* qp = p.q + ((int64_t)(si.q0 + qrow) * p.hq + head) * kHeadDim + gi * 64;
 #pragma unroll
-  for (int cb = 0; cb < kCB; ++cb) {
-    const int pair = wave * (kCB * 32) + cb * 32 + col;
-    const int prow = pair / p.gwg;
-    const int head_in_group = ht * p.gwg + (pair - prow * p.gwg);
-    col_ok[cb] = prow < rows_here && pair < p.bm * p.gwg && head_in_group < p.group;
-    qrow[cb] = r0 + prow;
-    head[cb] = kvh * p.group + head_in_group;
-    row_lim[cb] = qrow[cb] + offset;  // last visible key (causal)
-    if (col_ok[cb]) {
-      const uint16_t* qp =
-          p.q + ((int64_t)(si.q0 + qrow[cb]) * p.hq + head[cb]) * kHeadDim + gi * 64;
+    for (int st = 0; st < 8; ++st) qf[st] = ldg16(qp + 8 * st);
+  } else {
 #pragma unroll
-      for (int st = 0; st < 8; ++st) qf[cb][st] = ldg16(qp + 8 * st);
-    } else {
-#pragma unroll
-      for (int st = 0; st < 8; ++st) qf[cb][st] = u32x4_t{0, 0, 0, 0};
-    }
+    for (int st = 0; st < 8; ++st) qf[st] = u32x4_t{0, 0, 0, 0};
   }
 
-  f32x16_t acc[kCB][4];
+  f32x16_t acc[4];
 #pragma unroll
-  for (int cb = 0; cb < kCB; ++cb)
-#pragma unroll
-    for (int d = 0; d < 4; ++d) acc[cb][d] = f32x16_t{};
-  float m[kCB], lsum[kCB];
-#pragma unroll
-  for (int cb = 0; cb < kCB; ++cb) { m[cb] = -INFINITY; lsum[cb] = 0.f; }
+  for (int d = 0; d < 4; ++d) acc[d] = f32x16_t{};
+  // Online softmax state of this column: m is the reference (base 2, scaled)
+  // the exponentials are taken against, negm = -m for the exponent FMA; +inf
+  // until the first visible key, which forces the first update.
+  float m = -INFINITY, negm = INFINITY, lsum = 0.f;
   // smallest visible-key limit among the work-group's rows: tiles past it need masks
   const int wg_min_lim = r0 + offset;
+
+  // LDS byte offsets of this lane's fragments within one buffer (the buffer
+  // and the 32-key half add compile-time offsets).  K: chunk 8*gi + st of
+  // row col (the XOR swizzle depends on the row mod 16 only).  V^T: the
+  // transpose-read addresses of rows 4*gi + i16/4 (a = 0) and +8 (a = 1),
+  // 16-dim group d of the 32-dim block, 8-byte half i16 % 2.
+  int koff[8], voff[4][2];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) koff[st] = swz_off(col, 8 * gi + st);
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int r = 4 * gi + (i16 >> 2) + 8 * a;
+      const int c = 4 * d + 2 * g16 + ((i16 & 3) >> 1);
+      voff[d][a] = kTileBytes + swz_off(r, c) + 8 * (i16 & 1);
+    }
 
   // Paged K/V: the sequence's page ids for keys [0, kv_end), staged per window
   // of kPidWin pages (invalid ids become -1).
@@ -379,16 +391,17 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
   if (PAGED) stage_pids(wbase);
   __syncthreads();
 
-  if (kt1 > kt0) {
-    unsigned char* k0 = smem + (kt0 & 1) * 2 * kTileBytes;
-    issue_tile<PAGED, LAYOUT>(p, si, kvh, kt0, wave, lane, pids, wbase, k0, k0 + kTileBytes);
-  }
+  // Tile kt0 goes to buffer 0, kt0 + 1 to buffer 1, and so on.
+  if (kt1 > kt0)
+    issue_tile<PAGED, LAYOUT>(p, si, kvh, kt0, wave, lane, pids, wbase, smem, smem + kTileBytes);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const unsigned char* ks = smem + (kt & 1) * 2 * kTileBytes;
-    const unsigned char* vs = ks + kTileBytes;
+  // One 64-key tile from LDS buffer BUF (a compile-time constant, so every
+  // fragment address is a per-lane register plus an immediate offset).
+  auto tile_step = [&](int kt, auto buf_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    const unsigned char* ks = smem + BUF * 2 * kTileBytes;
     if (PAGED && kt + 1 < kt1 && (kt + 1) % kTilesPerWin == 0) {
       // the next tile starts a new page-id window (only tile kt+1 uses page
       // ids from here on, and every wave is past its reads of the old window)
@@ -398,7 +411,7 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
       __syncthreads();
     }
     if (kt + 1 < kt1) {  // tile kt+1 streams into the other buffer meanwhile
-      unsigned char* kn = smem + ((kt + 1) & 1) * 2 * kTileBytes;
+      unsigned char* kn = smem + (1 - BUF) * 2 * kTileBytes;
       issue_tile<PAGED, LAYOUT>(p, si, kvh, kt + 1, wave, lane, pids, wbase, kn, kn + kTileBytes);
     }
 
@@ -408,128 +421,129 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       // S^T[key][col] for keys 32*mb .. +31: 8 k-steps over the 128 dims
-      // paged kernel: waves in a matrix phase issue first (measured 1.5 %
-      // faster there; the ragged kernel measured slower and keeps one priority)
+      // paged kernel: waves in a matrix phase issue first (measured faster
+      // there; the ragged kernel measured slower and keeps one priority)
       if constexpr (PAGED) __builtin_amdgcn_s_setprio(1);
-      f32x16_t s[kCB];
-#pragma unroll
-      for (int cb = 0; cb < kCB; ++cb) s[cb] = f32x16_t{};
+      f32x16_t s = f32x16_t{};
       if constexpr (PAGED) {
         // all 8 K fragments read before the MFMAs (scheduling groups): the
         // paged kernel measured faster this way, the ragged one does not
         u32x4_t kf[8];
 #pragma unroll
         for (int st = 0; st < 8; ++st)
-          kf[st] = *reinterpret_cast<const u32x4_t*>(ks + swz_off(mb * 32 + col, 8 * gi + st));
+          kf[st] = *reinterpret_cast<const u32x4_t*>(ks + mb * 8192 + koff[st]);
 #pragma unroll
-        for (int st = 0; st < 8; ++st)
-#pragma unroll
-          for (int cb = 0; cb < kCB; ++cb) s[cb] = mfma_32x32x16(kf[st], qf[cb][st], s[cb]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);        // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 8 * kCB, 0);  // then MFMAs
+        for (int st = 0; st < 8; ++st) s = mfma_32x32x16(kf[st], qf[st], s);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // then MFMAs
       } else {
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
-          const u32x4_t a =
-              *reinterpret_cast<const u32x4_t*>(ks + swz_off(mb * 32 + col, 8 * gi + st));
-#pragma unroll
-          for (int cb = 0; cb < kCB; ++cb) s[cb] = mfma_32x32x16(a, qf[cb][st], s[cb]);
-        }
+        for (int st = 0; st < 8; ++st)
+          s = mfma_32x32x16(*reinterpret_cast<const u32x4_t*>(ks + mb * 8192 + koff[st]), qf[st],
+                            s);
       }
       if constexpr (PAGED) __builtin_amdgcn_s_setprio(0);
-      uint32_t pk[kCB][8];
+      // V^T fragments of this half, read now so that their LDS latency passes
+      // under the softmax (they do not depend on it).  Transpose read: lanes
+      // 4e..4e+3 of a 16-lane group address row (32*mb + 16*h + 4*(l/32) + e)
+      // (then +8), 16 dims of the 32-wide d block.
+      u32x4_t vf[2][4];
 #pragma unroll
-      for (int cb = 0; cb < kCB; ++cb) {
-        float mraw = -INFINITY;
-        if (need_mask) {
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + mb * 32 + 8 * (r >> 2) + 4 * gi + (r & 3);
-            const bool vis = key < si.klen && (!p.causal || key <= row_lim[cb]);
-            s[cb][r] = vis ? s[cb][r] : -INFINITY;
-            mraw = fmaxf(mraw, s[cb][r]);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, s[cb][r]);
+        for (int d = 0; d < 4; ++d) {
+          const unsigned char* vb = ks + 32 * mb * 256 + 16 * h * 256;
+          const u32x2_t a0 = lds_read_tr16(reinterpret_cast<const uint16_t*>(vb + voff[d][0]));
+          const u32x2_t a1 = lds_read_tr16(reinterpret_cast<const uint16_t*>(vb + voff[d][1]));
+          vf[h][d] = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
         }
-        // raw-score max (the scale is >= 0, so it commutes with max), then
-        // lazy rescaling: the reference max moves only when exceeded by 2^8
-        // (a block with no visible key keeps -inf, also for a zero scale)
+      __builtin_amdgcn_sched_barrier(0);
+      // Probabilities against the current reference, packed to bf16 pairs
+      // (the P operand) and summed in f32; masked keys weigh exactly 0
+      // (selected, not computed: with a zero scale fmaf(-inf, 0, x) is NaN).
+      // The masked form is a separate instance so the common tiles carry none
+      // of its selects.
+      uint32_t pk[8];
+      float psum;
+      auto probs = [&](auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value != 0;
+        psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float p0 = fast_exp2(fmaf(s[r], p.scale_log2, negm));
+          float p1 = fast_exp2(fmaf(s[r + 1], p.scale_log2, negm));
+          if constexpr (MASKED) {
+            p0 = s[r] == -INFINITY ? 0.f : p0;
+            p1 = s[r + 1] == -INFINITY ? 0.f : p1;
+          }
+          pk[r >> 1] = pack_bf16x2(p0, p1);
+          psum += p0 + p1;
+        }
+      };
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + mb * 32 + 8 * (r >> 2) + 4 * gi + (r & 3);
+          const bool vis = (key < si.klen) & (!p.causal | (key <= row_lim));
+          s[r] = vis ? s[r] : -INFINITY;
+        }
+        probs(BufTag<1>{});
+      } else {
+        probs(BufTag<0>{});
+      }
+      // Lazy reference: it moves only when this lane's 16 weights sum past
+      // 2^8 (or are not finite: the first visible key, against m = -inf).
+      // Then every column takes its exact running max (raw-score max times
+      // the scale, which commutes with a scale >= 0), rescales its state and
+      // recomputes.  The result is the same softmax: the reference cancels
+      // in o = acc / l.
+      if (__builtin_amdgcn_ballot_w64(!(psum <= 256.f)) != 0) {
+        float mraw = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mraw = fmaxf(mraw, s[r]);
         const float mred = pair_max32(mraw);
+        // a column with no visible key keeps -inf (also for a zero scale)
         const float mt = mred == -INFINITY ? -INFINITY : mred * p.scale_log2;
-        if (__builtin_amdgcn_ballot_w64(mt > m[cb] + 8.f) != 0) {
-          const float mnew = mt > m[cb] + 8.f ? mt : m[cb];
-          const float corr = fast_exp2(m[cb] - mnew);  // 0 while m is still -inf
-          lsum[cb] *= corr;
+        if (mt > m) {
+          const float corr = fast_exp2(m - mt);  // 0 while m is still -inf
+          lsum *= corr;
 #pragma unroll
           for (int d = 0; d < 4; ++d)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[cb][d][r] *= corr;
-          m[cb] = mnew;
+            for (int r = 0; r < 16; ++r) acc[d][r] *= corr;
+          m = mt;
+          negm = -mt;
         }
-        const float muse = m[cb] == -INFINITY ? 0.f : m[cb];
-        float psum = 0.f;
-        if (need_mask) {
-          // masked keys weigh exactly 0: with a zero scale fmaf(-inf, 0, x)
-          // is NaN, so the weight is selected, not computed
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            float p0 = fast_exp2(fmaf(s[cb][r], p.scale_log2, -muse));
-            float p1 = fast_exp2(fmaf(s[cb][r + 1], p.scale_log2, -muse));
-            p0 = s[cb][r] == -INFINITY ? 0.f : p0;
-            p1 = s[cb][r + 1] == -INFINITY ? 0.f : p1;
-            psum += p0 + p1;
-            pk[cb][r >> 1] = pack_bf16x2(p0, p1);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            const float p0 = fast_exp2(fmaf(s[cb][r], p.scale_log2, -muse));
-            const float p1 = fast_exp2(fmaf(s[cb][r + 1], p.scale_log2, -muse));
-            psum += p0 + p1;
-            pk[cb][r >> 1] = pack_bf16x2(p0, p1);
-          }
-        }
-        lsum[cb] += psum;
+        if (need_mask)
+          probs(BufTag<1>{});
+        else
+          probs(BufTag<0>{});
       }
+      lsum += psum;
       if constexpr (PAGED) __builtin_amdgcn_s_setprio(1);
       // O^T += V^T * P^T over the 2 k-steps of 16 keys in this block.
-      // Transpose read: lanes 4e..4e+3 of
-      // a 16-lane group address row (32*mb + 16*h + 4*(l/32) + e) (then +8),
-      // 16 dims of the 32-wide d block.
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int r = 32 * mb + 16 * h + 4 * gi + (i16 >> 2);
-        const int b8 = 8 * (i16 & 1);
+        const u32x4_t pf = u32x4_t{pk[4 * h], pk[4 * h + 1], pk[4 * h + 2], pk[4 * h + 3]};
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const int c = 4 * d + 2 * g16 + ((i16 & 3) >> 1);
-          const u32x2_t a0 = lds_read_tr16(reinterpret_cast<const uint16_t*>(vs + swz_off(r, c) + b8));
-          const u32x2_t a1 = lds_read_tr16(reinterpret_cast<const uint16_t*>(vs + swz_off(r + 8, c) + b8));
-          const u32x4_t a = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
-#pragma unroll
-          for (int cb = 0; cb < kCB; ++cb) {
-            const u32x4_t pf = u32x4_t{pk[cb][4 * h], pk[cb][4 * h + 1], pk[cb][4 * h + 2],
-                                       pk[cb][4 * h + 3]};
-            acc[cb][d] = mfma_32x32x16(a, pf, acc[cb][d]);
-          }
-        }
+        for (int d = 0; d < 4; ++d) acc[d] = mfma_32x32x16(vf[h][d], pf, acc[d]);
       }
     }
 
     if constexpr (PAGED) __builtin_amdgcn_s_setprio(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile kt+1 has landed in LDS
     __syncthreads();
+  };
+  for (int kt = kt0; kt < kt1; kt += 2) {
+    tile_step(kt, BufTag<0>{});
+    if (kt + 1 < kt1) tile_step(kt + 1, BufTag<1>{});
   }
 
-#pragma unroll
-  for (int cb = 0; cb < kCB; ++cb) {
-    const float ls = pair_sum32(lsum[cb]);
-    if (!col_ok[cb]) continue;
+  const float ls = pair_sum32(lsum);
+  if (col_ok) {
     const float inv = ls > 0.f ? 1.f / ls : 0.f;
-    const int64_t hrow = (int64_t)(si.q0 + qrow[cb]) * p.hq + head[cb];
-    const float lse_val = ls > 0.f ? (m[cb] + __log2f(ls)) * kLn2 : -INFINITY;
+    const int64_t hrow = (int64_t)(si.q0 + qrow) * p.hq + head;
+    const float lse_val = ls > 0.f ? (m + __log2f(ls)) * kLn2 : -INFINITY;
     if (SPLIT) {  // this chunk's normalised state, f32
       const int64_t srow = (int64_t)chunk * p.nnz_qo * p.hq + hrow;
       float* wrow = p.ws_o + srow * kHeadDim;
@@ -538,27 +552,26 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < 16; r += 4) {
           const int dd = 32 * d + 8 * (r >> 2) + 4 * gi;
-          const u32x4_t w = {__float_as_uint(acc[cb][d][r] * inv),
-                             __float_as_uint(acc[cb][d][r + 1] * inv),
-                             __float_as_uint(acc[cb][d][r + 2] * inv),
-                             __float_as_uint(acc[cb][d][r + 3] * inv)};
+          const u32x4_t w = {__float_as_uint(acc[d][r] * inv), __float_as_uint(acc[d][r + 1] * inv),
+                             __float_as_uint(acc[d][r + 2] * inv),
+                             __float_as_uint(acc[d][r + 3] * inv)};
           *reinterpret_cast<u32x4_t*>(wrow + dd) = w;
         }
       if (gi == 0) p.ws_lse[srow] = lse_val;
-      continue;
+    } else {
+      uint16_t* orow = p.o + hrow * kHeadDim;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          const int dd = 32 * d + 8 * (r >> 2) + 4 * gi;
+          u32x2_t w;
+          w[0] = pack_bf16x2(acc[d][r] * inv, acc[d][r + 1] * inv);
+          w[1] = pack_bf16x2(acc[d][r + 2] * inv, acc[d][r + 3] * inv);
+          *reinterpret_cast<u32x2_t*>(orow + dd) = w;
+        }
+      if (gi == 0 && p.lse != nullptr) p.lse[hrow] = lse_val;
     }
-    uint16_t* orow = p.o + hrow * kHeadDim;
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; r += 4) {
-        const int dd = 32 * d + 8 * (r >> 2) + 4 * gi;
-        u32x2_t w;
-        w[0] = pack_bf16x2(acc[cb][d][r] * inv, acc[cb][d][r + 1] * inv);
-        w[1] = pack_bf16x2(acc[cb][d][r + 2] * inv, acc[cb][d][r + 3] * inv);
-        *reinterpret_cast<u32x2_t*>(orow + dd) = w;
-      }
-    if (gi == 0 && p.lse != nullptr) p.lse[hrow] = lse_val;
   }
   __syncthreads();  // LDS (tiles, page ids, selection) is reused by the next item
   }
