@@ -72,6 +72,31 @@ class LaunchTimer:
         return np.array([a.elapsed_time(b) for a, b in self.pairs[:n]])
 
 
+def warm_clock(torch, fn, seconds=0.3):
+    """Call fn until `seconds` of wall time have passed: the GPU's clock ramps
+    up under sustained load, and the extra rows are timed at its steady state."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+
+
+def cold_launch_samples(torch, stream, fn, n, scratch):
+    """n launches of fn, each between its own event pair, with a 1 GiB scratch
+    write before each (outside the pair) so the launch finds caches cold.
+    Returns the per-launch durations in ms."""
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n)]
+    for i, (a, b) in enumerate(pairs):
+        scratch.fill_(i & 0xff)
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in pairs])
+
+
 def decode_bytes(case):
     """Algorithmic HBM bytes of one paged decode: K+V rows of every token of every
     sequence and kv head, q in, o out, and the page table read."""
@@ -114,8 +139,14 @@ def profiled_traffic(kernel_file, profile_name):
 
 # ----------------------------------------------------------------------------- rows
 
-def bench_decode(torch, oxa, W, case, steps, warmup, copies_bytes=1 << 30, partitions=None):
-    """Time paged decode over `case`, rotating pool copies so each step is cold."""
+def bench_decode(torch, oxa, W, case, steps, warmup, scratch, copies_bytes=1 << 30,
+                 partitions=None, cold_launches=100):
+    """Time paged decode over `case`: `steps` launches back to back between one
+    event pair, each reading another copy of the KV pool (copies rotate, > 1
+    GiB in all, so every step streams its KV from HBM), then `cold_launches`
+    more, each between its own event pair after a 1 GiB cache-flushing write,
+    for the per-launch distribution.  Every call passes the per-sequence
+    status array (the full operator contract)."""
     kv = case.kv
     B, hq, _ = case.q.shape
     P = case.num_partitions if partitions is None else partitions
@@ -128,6 +159,7 @@ def bench_decode(torch, oxa, W, case, steps, warmup, copies_bytes=1 << 30, parti
         vps.append(vps[0].clone())
     q = dev(case.q)
     o = torch.empty_like(q)
+    status = torch.empty(B, dtype=torch.int32, device="cuda")
     indptr, ids, lens = dev(kv.page_indptr), dev(kv.page_indices), dev(kv.seq_lens)
     nbytes = oxa.oxa_paged_decode_workspace_bytes(B, hq, P)
     ws = torch.empty(max(nbytes, 4) // 4, dtype=torch.float32, device="cuda") if nbytes else None
@@ -138,7 +170,7 @@ def bench_decode(torch, oxa, W, case, steps, warmup, copies_bytes=1 << 30, parti
         rc = oxa.oxa_paged_decode(q, kps[j], vps[j], indptr, ids, lens, o,
                                   max_seq_len=case.max_seq_len, sm_scale=case.sm_scale,
                                   layout=kv.layout, num_kv_heads=kv.num_kv_heads,
-                                  num_partitions=P, workspace=ws)
+                                  num_partitions=P, workspace=ws, status=status)
         if rc != 0:
             raise RuntimeError(oxa.status_string(rc))
 
@@ -154,12 +186,12 @@ def bench_decode(torch, oxa, W, case, steps, warmup, copies_bytes=1 << 30, parti
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    # spread: the same launches again, each between its own event pair (the
-    # event records add a few us per launch, so these are not the throughput)
-    timer = LaunchTimer(torch, stream, steps)
-    timer.run(lambda i: call(i + warmup + steps), steps)
-    launch = timer.launch_ms(steps)
-    return dict(total_ms=total_ms, launch_ms=launch, bytes=decode_bytes(case), copies=ncopies,
+    assert (status == 0).all().item(), "decode status reports an invalid sequence"
+    # distribution: cold launches, each between its own event pair (an event
+    # record before and after a launch adds a few us to it)
+    cold = cold_launch_samples(torch, stream, lambda i: call(i + warmup + steps),
+                               max(cold_launches, steps), scratch)
+    return dict(total_ms=total_ms, launch_ms=cold, bytes=decode_bytes(case), copies=ncopies,
                 partitions=P, steps=steps)
 
 
@@ -180,6 +212,7 @@ def bench_prefill_ragged(torch, oxa, case, iters, warmup):
 
     for i in range(warmup):
         call(i)
+    warm_clock(torch, lambda: call(0))
     timer = LaunchTimer(torch, stream, iters)
     timer.run(call, iters)
     ms = timer.launch_ms(iters)
@@ -223,9 +256,12 @@ def bench_append_and_paged_prefill(torch, oxa, case, iters, warmup):
     for i in range(warmup):
         append(i)
         prefill(i)
+    warm_clock(torch, lambda: prefill(0), seconds=0.2)
+    warm_clock(torch, lambda: append(0), seconds=0.1)
     ta = LaunchTimer(torch, stream, iters)
     ta.run(append, iters)
     a_ms = ta.launch_ms(iters)
+    warm_clock(torch, lambda: prefill(0), seconds=0.1)
     tp = LaunchTimer(torch, stream, iters)
     tp.run(prefill, iters)
     p_ms = tp.launch_ms(iters)
@@ -242,6 +278,7 @@ def bench_append_and_paged_prefill(torch, oxa, case, iters, warmup):
 
     for i in range(warmup):
         plain(i)
+    warm_clock(torch, lambda: plain(0), seconds=0.1)
     tq = LaunchTimer(torch, stream, iters)
     tq.run(plain, iters)
     q_ms = tq.launch_ms(iters)
@@ -262,16 +299,16 @@ def bench_pages_shapes(torch, oxa, W, iters=200, warmup=20):
     """Per-call latency of the four attention shapes that the Oxide Infer README's
     Performance snapshot prints (HIP events around each launch, inputs resident,
     so small working sets sit in cache, as in a serving loop).  Head counts are
-    not printed there: 32 q heads, 32 kv heads for MHA and 8 for GQA4."""
+    not printed there: 32 q heads, 32 kv heads for MHA and 8 for GQA4.
+
+    A prefill shape is timed with the optional workspace (small calls may then
+    split their keys) and without it ("_unsplit"), the two forms alternating
+    call by call so that both see the same clock; the pair is timed twice, in
+    both orders, and each form reports the median over both passes."""
     stream = torch.cuda.current_stream()
     res = {}
 
-    def timed(name, call):
-        for i in range(warmup):
-            call(i)
-        t = LaunchTimer(torch, stream, iters)
-        t.run(call, iters)
-        ms = t.launch_ms(iters)
+    def graph_us(call):
         # the same call captured once in a HIP graph and replayed
         side = torch.cuda.Stream()
         side.wait_stream(stream)
@@ -287,10 +324,32 @@ def bench_pages_shapes(torch, oxa, W, iters=200, warmup=20):
             g.replay()
         tg = LaunchTimer(torch, stream, iters)
         tg.run(lambda i: g.replay(), iters)
-        gms = tg.launch_ms(iters)
-        res[name] = {"us_median": round(float(np.median(ms)) * 1e3, 2),
-                     "us_mean": round(float(np.mean(ms)) * 1e3, 2),
-                     "graph_us_median": round(float(np.median(gms)) * 1e3, 2)}
+        return round(float(np.median(tg.launch_ms(iters))) * 1e3, 2)
+
+    def timed(forms):
+        """forms: [(name, call)]; calls alternate within each pass."""
+        for _, call in forms:
+            for i in range(warmup):
+                call(i)
+        warm_clock(torch, lambda: [c(0) for _, c in forms], seconds=0.2)
+        samples = {name: [] for name, _ in forms}
+        for order in (forms, forms[::-1]):
+            pairs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in order] for _ in range(iters)]
+            for i in range(iters):
+                for (name, call), (a, b) in zip(order, pairs[i]):
+                    a.record(stream)
+                    call(i)
+                    b.record(stream)
+            torch.cuda.synchronize()
+            for i in range(iters):
+                for (name, _), (a, b) in zip(order, pairs[i]):
+                    samples[name].append(a.elapsed_time(b))
+        for name, call in forms:
+            ms = np.array(samples[name])
+            res[name] = {"us_median": round(float(np.median(ms)) * 1e3, 2),
+                         "us_p10_p90": [round(float(x) * 1e3, 2) for x in np.percentile(ms, [10, 90])],
+                         "graph_us_median": graph_us(call)}
 
     def check(rc):
         if rc != 0:
@@ -302,12 +361,12 @@ def bench_pages_shapes(torch, oxa, W, iters=200, warmup=20):
     o = torch.empty_like(q)
     args = (dev(kv.k_pool), dev(kv.v_pool), dev(kv.page_indptr), dev(kv.page_indices),
             dev(kv.seq_lens))
-    timed("decode_mha_b1_kv1", lambda i: check(oxa.oxa_paged_decode(
+    timed([("decode_mha_b1_kv1", lambda i: check(oxa.oxa_paged_decode(
         q, *args, o, max_seq_len=1, sm_scale=c.sm_scale, layout=kv.layout,
-        num_kv_heads=kv.num_kv_heads)))
+        num_kv_heads=kv.num_kv_heads)))])
 
     # prefill calls pass the optional workspace, with which small calls split
-    # their keys over more CUs; the "_unsplit" rows time the same calls without
+    # their keys over more CUs; the "_unsplit" forms are the same calls without
     def workspace(nbytes):
         return torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
 
@@ -319,12 +378,12 @@ def bench_pages_shapes(torch, oxa, W, iters=200, warmup=20):
         mq, mk = int(np.diff(rc_.qo_indptr).max()), int(np.diff(rc_.kv_indptr).max())
         ws = workspace(oxa.oxa_ragged_prefill_workspace_bytes(len(rc_.qo_indptr) - 1,
                                                               qr.shape[0], qr.shape[1]))
-        for suffix, w in (("", ws), ("_unsplit", None)):
-            timed(name + suffix,
-                  lambda i, qr=qr, kr=kr, vr=vr, orr=orr, qi=qi, ki=ki, mq=mq, mk=mk, c=rc_, w=w:
-                  check(oxa.oxa_ragged_prefill(qr, kr, vr, qi, ki, orr, max_qo_len=mq,
-                                               max_kv_len=mk, sm_scale=c.sm_scale, causal=True,
-                                               workspace=w)))
+        timed([(name + suffix,
+                lambda i, qr=qr, kr=kr, vr=vr, orr=orr, qi=qi, ki=ki, mq=mq, mk=mk, c=rc_, w=w:
+                check(oxa.oxa_ragged_prefill(qr, kr, vr, qi, ki, orr, max_qo_len=mq,
+                                             max_kv_len=mk, sm_scale=c.sm_scale, causal=True,
+                                             workspace=w)))
+               for suffix, w in (("", ws), ("_unsplit", None))])
 
     pc = W.pages_paged_gqa4()
     kv = pc.kv
@@ -333,10 +392,10 @@ def bench_pages_shapes(torch, oxa, W, iters=200, warmup=20):
     pargs = (dev(pc.qo_indptr), dev(kv.k_pool), dev(kv.v_pool), dev(kv.page_indptr),
              dev(kv.page_indices), dev(kv.seq_lens))
     ws = workspace(oxa.oxa_paged_prefill_workspace_bytes(2, qp.shape[0], qp.shape[1]))
-    for suffix, w in (("", ws), ("_unsplit", None)):
-        timed("paged_gqa4_q32+64_kv256+1024" + suffix, lambda i, w=w: check(oxa.oxa_paged_prefill(
-            qp, *pargs, op, max_qo_len=64, max_seq_len=1024, sm_scale=pc.sm_scale,
-            layout=kv.layout, num_kv_heads=kv.num_kv_heads, causal=True, workspace=w)))
+    timed([("paged_gqa4_q32+64_kv256+1024" + suffix, lambda i, w=w: check(oxa.oxa_paged_prefill(
+        qp, *pargs, op, max_qo_len=64, max_seq_len=1024, sm_scale=pc.sm_scale,
+        layout=kv.layout, num_kv_heads=kv.num_kv_heads, causal=True, workspace=w)))
+           for suffix, w in (("", ws), ("_unsplit", None))])
     return res
 
 
@@ -351,6 +410,7 @@ def bench_merge(torch, oxa, iters=30, warmup=5):
         bufs = [make(i) for i in range(2)]
         for i in range(warmup):
             call(bufs[i % 2])
+        warm_clock(torch, lambda: call(bufs[0]), seconds=0.1)
         t = LaunchTimer(torch, stream, iters)
         t.run(lambda i: call(bufs[i % 2]), iters)
         ms = float(np.mean(t.launch_ms(iters)))
@@ -402,6 +462,7 @@ def bench_rope(torch, oxa, iters=20, warmup=3):
 
     for i in range(warmup):
         call(i)
+    warm_clock(torch, lambda: call(0), seconds=0.1)
     t = LaunchTimer(torch, stream, iters)
     t.run(call, iters)
     ms = float(np.mean(t.launch_ms(iters)))
@@ -412,25 +473,98 @@ def bench_rope(torch, oxa, iters=20, warmup=3):
                                             "bytes": nbytes}}
 
 
-def cpu_baseline(case, budget_s=10.0):
-    """The oracle's paged decode of the whole workload, repeated for ~budget_s,
-    with its BLAS pool held to one thread."""
-    from oracle import attention as A
-    from threadpoolctl import threadpool_limits
-    kv = case.kv
-    reps, t0 = 0, time.perf_counter()
-    with threadpool_limits(limits=1):
-        while True:
-            A.paged_decode(case.q, kv.k_pool, kv.v_pool, kv.layout, kv.page_indptr,
-                           kv.page_indices, kv.seq_lens, case.sm_scale)
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= budget_s:
+def host_info():
+    """Host cores, the BLAS pool's threads and the CPU model string."""
+    from threadpoolctl import threadpool_info
+    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
                 break
-    gbs = decode_bytes(case) * reps / el / 1e9
-    return dict(value=round(gbs, 3), unit="GB/s", cores=1, kind="oracle",
-                sample=f"whole batch-32 GQA4 decode workload, {reps} repetitions in {el:.1f} s, "
-                       "numpy float64, BLAS held to 1 thread")
+    except OSError:
+        pass
+    return {"cpu_count": os.cpu_count(), "blas_threads": max(blas) if blas else 1,
+            "cpu_model": model}
+
+
+def cpu_baseline(cases):
+    """The oracle (float64 numpy, as it stands) timed on this host's cores, its
+    BLAS pool at its default size, on each workload or a stated sample of it:
+    paged decode (batch-1 MHA, batch-32 GQA4, long MQA) median of 5 whole
+    runs; ragged GQA4 prefill, RoPE + append and the long paged prefill once
+    each on a sample (rates scaled by the sample's share of the work)."""
+    from oracle import attention as A
+    from oracle import rope as R
+    import workloads as W
+    info = host_info()
+    out = {}
+
+    def med5(fn):
+        ts = []
+        for _ in range(5):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
+
+    for name, key in (("decode_mha_b1_l256", "c1"), ("decode_gqa4_b32", "c2"),
+                      ("decode_mqa_b8_l32768", "c3")):
+        case = cases[key]
+        kv = case.kv
+        t = med5(lambda: A.paged_decode(case.q, kv.k_pool, kv.v_pool, kv.layout, kv.page_indptr,
+                                        kv.page_indices, kv.seq_lens, case.sm_scale))
+        out[name] = {"s": round(t, 4), "GB/s": round(decode_bytes(case) / t / 1e9, 3),
+                     "sample": "whole workload, median of 5"}
+    rng = np.random.default_rng(7)
+    c4 = cases["c4"]
+    rows = np.sort(rng.choice(len(c4.q), 256, replace=False))
+    qlens, klens = np.diff(c4.qo_indptr), np.diff(c4.kv_indptr)
+    t0 = time.perf_counter()
+    A.ragged_prefill(c4.q, c4.k, c4.v, c4.qo_indptr, c4.kv_indptr, c4.sm_scale, True, rows=rows)
+    t = time.perf_counter() - t0
+    fl = sampled_causal_flops(rows, c4.qo_indptr, klens, c4.num_qo_heads)
+    out["prefill_ragged_gqa4_4seq"] = {"s": round(t, 3), "GFLOP/s": round(fl / t / 1e9, 3),
+                                       "sample": "256 random query rows of 7680 (all heads)"}
+    c5 = cases["c5"]
+    small = W.append_case(1005, seq_lens=[1024, 1024], num_qo_heads=32, num_kv_heads=8)
+    kv = small.kv
+    t0 = time.perf_counter()
+    R.paged_append_rope(small.q, small.k, small.v, small.batch_indices, small.positions,
+                        kv.k_pool, kv.v_pool, kv.layout, kv.page_indptr, kv.page_indices,
+                        small.page_refcounts, small.rope_theta)
+    t = time.perf_counter() - t0
+    nbytes = 2048 * (32 * 256 * 2 + 8 * 256 * 4 + 8) + 128 * 8
+    out["rope_append_2x16384"] = {"s": round(t, 3), "GB/s": round(nbytes / t / 1e9, 4),
+                                  "sample": "2 x 1024 tokens of the same shape (32 q / 8 kv "
+                                            "heads, exclusive pages)"}
+    kv = c5.kv
+    rows = np.sort(rng.choice(len(c5.q), 64, replace=False))
+    t0 = time.perf_counter()
+    A.paged_prefill(c5.q, c5.qo_indptr, kv.k_pool, kv.v_pool, kv.layout, kv.page_indptr,
+                    kv.page_indices, kv.seq_lens, c5.sm_scale, True, rows=rows)
+    t = time.perf_counter() - t0
+    fl = sampled_causal_flops(rows, c5.qo_indptr, kv.seq_lens, 32)
+    out["prefill_paged_gqa4_2x16384"] = {"s": round(t, 3), "GFLOP/s": round(fl / t / 1e9, 3),
+                                         "sample": "64 random query rows of 32768 (all heads)"}
+    c2 = out["decode_gqa4_b32"]
+    return dict(value=c2["GB/s"], unit="GB/s", cores=info["blas_threads"], kind="oracle",
+                sample="whole batch-32 GQA4 decode workload, median of 5 runs (numpy float64, "
+                       "BLAS pool at its default size; the other workloads under 'configs')",
+                host=info, configs=out)
+
+
+def sampled_causal_flops(rows, qo_indptr, kv_lens, hq, d=128):
+    """Matrix flops of the given packed query rows (bottom-right causal)."""
+    qo_indptr = np.asarray(qo_indptr)
+    total = 0
+    for r in rows:
+        b = int(np.searchsorted(qo_indptr, r, side="right")) - 1
+        qlen = int(qo_indptr[b + 1] - qo_indptr[b])
+        i = int(r - qo_indptr[b])
+        total += i + 1 + int(kv_lens[b]) - qlen
+    return 4 * d * hq * total
 
 
 # ----------------------------------------------------------------------------- main
@@ -464,23 +598,29 @@ def main():
     decode_P = args.decode_partitions
     if decode_P is None:
         decode_P = int(os.environ.get("OXA_BENCH_DECODE_P", "1"))
-    case2 = W.decode_gqa4_batch(num_partitions=decode_P)
+    cases = {"c2": W.decode_gqa4_batch(num_partitions=decode_P)}
+    case2 = cases["c2"]
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")  # cache-flushing writes
     if only in (None, "decode"):
         log("decode: batch-32 GQA4")
-        out["decode"] = bench_decode(torch, oxa, W, case2, args.steps, args.warmup)
+        out["decode"] = bench_decode(torch, oxa, W, case2, args.steps, args.warmup, scratch)
     if only in (None, "decode_mha"):
         log("decode_mha: batch-1 MHA, 256 tokens")
-        out["decode_mha"] = bench_decode(torch, oxa, W, W.decode_mha_small(), 100, 10,
-                                         copies_bytes=1 << 30)
+        cases["c1"] = W.decode_mha_small()
+        out["decode_mha"] = bench_decode(torch, oxa, W, cases["c1"], 100, 10, scratch)
     if only in (None, "decode_mqa"):
         log("decode_mqa: batch-8 MQA, 32768 tokens, 16 partitions")
-        out["decode_mqa"] = bench_decode(torch, oxa, W, W.decode_mqa_long(), 30, 5)
+        cases["c3"] = W.decode_mqa_long()
+        out["decode_mqa"] = bench_decode(torch, oxa, W, cases["c3"], 30, 5, scratch)
     if only in (None, "prefill_ragged"):
         log("prefill_ragged: GQA4 {512,1024,2048,4096}")
-        out["prefill_ragged"] = bench_prefill_ragged(torch, oxa, W.ragged_gqa4_prefill(), 20, 3)
+        cases["c4"] = W.ragged_gqa4_prefill()
+        out["prefill_ragged"] = bench_prefill_ragged(torch, oxa, cases["c4"], 20, 3)
     if only in (None, "append", "prefill_paged"):
         log("append + paged prefill: 2 x 16384 tokens")
-        out["long"] = bench_append_and_paged_prefill(torch, oxa, W.rope_append_prefill(), 10, 2)
+        cases["c5"] = W.rope_append_prefill()
+        out["long"] = bench_append_and_paged_prefill(torch, oxa, cases["c5"], 10, 2)
+    del scratch
 
     if only in (None, "pages_shapes"):
         log("pages_shapes: the four printed attention shapes, per-call latency")
@@ -538,23 +678,33 @@ def main():
                          "kernel": "paged_decode_kernel" + ("" if r["partitions"] == 1 else
                                                             " + merge_states_kernel"),
                          "us_per_launch": round(step_ms * 1e3, 2),
-                         "per_launch_event_pairs_us_p10_p50_p90":
+                         "cold_launch_event_pairs_us_p10_p50_p90":
                              [round(float(x) * 1e3, 2) for x in
                               np.percentile(r["launch_ms"], [10, 50, 90])]},
         })
     rows = {}
+
+    def cold_stats(r):
+        ms = np.asarray(r["launch_ms"])
+        return {"cold_us_p10_p50_p90": [round(float(x) * 1e3, 2)
+                                        for x in np.percentile(ms, [10, 50, 90])],
+                "cold_us_samples": [round(float(x) * 1e3, 2) for x in ms]}
+
+    if "decode" in out:
+        rows["decode_gqa4_b32_cold_launches"] = cold_stats(out["decode"])
     if "decode_mha" in out:
         r = out["decode_mha"]
         lm = r["total_ms"] / r["steps"]
         rows["decode_mha_b1_l256"] = {"us": round(lm * 1e3, 2),
-                                      "GB/s": round(r["bytes"] / (lm * 1e-3) / 1e9, 1)}
+                                      "GB/s": round(r["bytes"] / (lm * 1e-3) / 1e9, 1),
+                                      **cold_stats(r)}
     if "decode_mqa" in out:
         r = out["decode_mqa"]
         lm = r["total_ms"] / r["steps"]
         gbs = r["bytes"] / (lm * 1e-3) / 1e9
         rows["decode_mqa_splitk_b8_l32768_p16"] = {
             "us": round(lm * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-            "bytes": r["bytes"]}
+            "bytes": r["bytes"], **cold_stats(r)}
     if "prefill_ragged" in out:
         r = out["prefill_ragged"]
         lm = float(np.mean(r["launch_ms"]))
@@ -599,7 +749,7 @@ def main():
         line.update({"value": None, "ms_per_step": None, "config": {"workload": only}})
     if only is None and not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        line["cpu_baseline"] = cpu_baseline(case2)
+        line["cpu_baseline"] = cpu_baseline(cases)
     print(json.dumps(line), flush=True)
 
 

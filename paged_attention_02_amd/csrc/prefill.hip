@@ -421,9 +421,6 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       // S^T[key][col] for keys 32*mb .. +31: 8 k-steps over the 128 dims
-      // paged kernel: waves in a matrix phase issue first (measured faster
-      // there; the ragged kernel measured slower and keeps one priority)
-      if constexpr (PAGED) __builtin_amdgcn_s_setprio(1);
       f32x16_t s = f32x16_t{};
       if constexpr (PAGED) {
         // all 8 K fragments read before the MFMAs (scheduling groups): the
@@ -442,7 +439,6 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
           s = mfma_32x32x16(*reinterpret_cast<const u32x4_t*>(ks + mb * 8192 + koff[st]), qf[st],
                             s);
       }
-      if constexpr (PAGED) __builtin_amdgcn_s_setprio(0);
       // V^T fragments of this half, read now so that their LDS latency passes
       // under the softmax (they do not depend on it).  Transpose read: lanes
       // 4e..4e+3 of a 16-lane group address row (32*mb + 16*h + 4*(l/32) + e)
@@ -520,7 +516,6 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
           probs(BufTag<0>{});
       }
       lsum += psum;
-      if constexpr (PAGED) __builtin_amdgcn_s_setprio(1);
       // O^T += V^T * P^T over the 2 k-steps of 16 keys in this block.
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -530,7 +525,6 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
       }
     }
 
-    if constexpr (PAGED) __builtin_amdgcn_s_setprio(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile kt+1 has landed in LDS
     __syncthreads();
   };
