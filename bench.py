@@ -35,8 +35,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, TFLOP/s
-ROWS = ("decode", "decode_mha", "decode_mqa", "prefill_ragged", "append", "prefill_paged",
-        "pages_shapes", "merge", "rope", "copy")
+ROWS = ("decode", "decode_mha", "decode_mqa", "decode_skewed", "prefill_ragged", "append",
+        "prefill_paged", "pages_shapes", "merge", "rope", "copy")
 
 
 def log(msg):
@@ -140,13 +140,14 @@ def profiled_traffic(kernel_file, profile_name):
 # ----------------------------------------------------------------------------- rows
 
 def bench_decode(torch, oxa, W, case, steps, warmup, scratch, copies_bytes=1 << 30,
-                 partitions=None, cold_launches=100):
+                 partitions=None, cold_launches=100, mode="direct"):
     """Time paged decode over `case`: `steps` launches back to back between one
     event pair, each reading another copy of the KV pool (copies rotate, > 1
     GiB in all, so every step streams its KV from HBM), then `cold_launches`
     more, each between its own event pair after a 1 GiB cache-flushing write,
     for the per-launch distribution.  Every call passes the per-sequence
-    status array (the full operator contract)."""
+    status array (the full operator contract).  mode "balanced" passes the
+    load-balanced mode's workspace."""
     kv = case.kv
     B, hq, _ = case.q.shape
     P = case.num_partitions if partitions is None else partitions
@@ -161,7 +162,11 @@ def bench_decode(torch, oxa, W, case, steps, warmup, scratch, copies_bytes=1 << 
     o = torch.empty_like(q)
     status = torch.empty(B, dtype=torch.int32, device="cuda")
     indptr, ids, lens = dev(kv.page_indptr), dev(kv.page_indices), dev(kv.seq_lens)
-    nbytes = oxa.oxa_paged_decode_workspace_bytes(B, hq, P)
+    if mode == "balanced":
+        nbytes = oxa.oxa_paged_decode_balanced_workspace_bytes(B, hq, P)
+        assert nbytes > 0
+    else:
+        nbytes = oxa.oxa_paged_decode_workspace_bytes(B, hq, P)
     ws = torch.empty(max(nbytes, 4) // 4, dtype=torch.float32, device="cuda") if nbytes else None
     stream = torch.cuda.current_stream()
 
@@ -604,6 +609,9 @@ def main():
     if only in (None, "decode"):
         log("decode: batch-32 GQA4")
         out["decode"] = bench_decode(torch, oxa, W, case2, args.steps, args.warmup, scratch)
+        log("decode: batch-32 GQA4, load-balanced mode")
+        out["decode_balanced"] = bench_decode(torch, oxa, W, case2, args.steps, args.warmup,
+                                              scratch, mode="balanced")
     if only in (None, "decode_mha"):
         log("decode_mha: batch-1 MHA, 256 tokens")
         cases["c1"] = W.decode_mha_small()
@@ -612,6 +620,15 @@ def main():
         log("decode_mqa: batch-8 MQA, 32768 tokens, 16 partitions")
         cases["c3"] = W.decode_mqa_long()
         out["decode_mqa"] = bench_decode(torch, oxa, W, cases["c3"], 30, 5, scratch)
+        log("decode_mqa: load-balanced mode")
+        out["decode_mqa_balanced"] = bench_decode(torch, oxa, W, cases["c3"], 30, 5, scratch,
+                                                  mode="balanced")
+    if only in (None, "decode_skewed"):
+        log("decode_skewed: batch-32 GQA4, one 32768-token sequence and 31 of 1024, both modes")
+        sk = W.decode_skewed()
+        out["decode_skewed"] = bench_decode(torch, oxa, W, sk, 30, 5, scratch, cold_launches=30)
+        out["decode_skewed_balanced"] = bench_decode(torch, oxa, W, sk, 30, 5, scratch,
+                                                     cold_launches=30, mode="balanced")
     if only in (None, "prefill_ragged"):
         log("prefill_ragged: GQA4 {512,1024,2048,4096}")
         cases["c4"] = W.ragged_gqa4_prefill()
@@ -698,13 +715,21 @@ def main():
         rows["decode_mha_b1_l256"] = {"us": round(lm * 1e3, 2),
                                       "GB/s": round(r["bytes"] / (lm * 1e-3) / 1e9, 1),
                                       **cold_stats(r)}
-    if "decode_mqa" in out:
-        r = out["decode_mqa"]
+    def decode_row(r):
         lm = r["total_ms"] / r["steps"]
         gbs = r["bytes"] / (lm * 1e-3) / 1e9
-        rows["decode_mqa_splitk_b8_l32768_p16"] = {
-            "us": round(lm * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-            "bytes": r["bytes"], **cold_stats(r)}
+        return {"us": round(lm * 1e3, 2), "GB/s": round(gbs, 1),
+                "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": r["bytes"], **cold_stats(r)}
+
+    if "decode_balanced" in out:
+        rows["decode_gqa4_b32_balanced_mode"] = decode_row(out["decode_balanced"])
+    if "decode_mqa" in out:
+        rows["decode_mqa_splitk_b8_l32768_p16"] = decode_row(out["decode_mqa"])
+        rows["decode_mqa_splitk_b8_l32768_p16_balanced_mode"] = decode_row(
+            out["decode_mqa_balanced"])
+    if "decode_skewed" in out:
+        rows["decode_skewed_gqa4_b32_direct_mode"] = decode_row(out["decode_skewed"])
+        rows["decode_skewed_gqa4_b32_balanced_mode"] = decode_row(out["decode_skewed_balanced"])
     if "prefill_ragged" in out:
         r = out["prefill_ragged"]
         lm = float(np.mean(r["launch_ms"]))

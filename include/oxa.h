@@ -87,7 +87,7 @@
 extern "C" {
 #endif
 
-#define OXA_ABI_VERSION 7
+#define OXA_ABI_VERSION 8
 #define OXA_PAGE_SIZE 16
 #define OXA_HEAD_DIM 128
 
@@ -275,6 +275,22 @@ oxa_status oxa_paged_decode_noalloc(
 /* Workspace bytes oxa_paged_decode needs (0 for num_partitions == 1). */
 size_t oxa_paged_decode_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t head_dim,
                                         int32_t num_partitions);
+
+/*
+ * Workspace bytes of oxa_paged_decode's load-balanced mode (0 when the shape
+ * has no such mode: batch * num_partitions > 2048).  A workspace of at least
+ * this size makes oxa_paged_decode cut the pages of all sequences (or of
+ * their partitions), laid end to end, into equal ranges, one per compute
+ * unit, and merge the pieces of the units a range boundary cuts in a second
+ * kernel, so a batch of mixed lengths takes the time of its total rather than
+ * of its longest sequence.  The results are those of the direct mode (the
+ * same attention, summed in another order), and with P > 1 the workspace
+ * starts with the same partition states; the rest of it is scratch.  Small
+ * calls (fewer than 64 pages of the largest possible total) take the direct
+ * mode whatever the workspace.
+ */
+size_t oxa_paged_decode_balanced_workspace_bytes(int32_t batch, int32_t num_qo_heads,
+                                                 int32_t head_dim, int32_t num_partitions);
 
 /*
  * Ragged prefill: sequence b's query rows q[qo_indptr[b] .. qo_indptr[b+1])

@@ -62,6 +62,7 @@ SIGNATURES = {
     "oxa_paged_decode": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _P, _P, _I, _P, _I, _F,
                               _I, _P, _Z, _P, _P, _P]),
     "oxa_paged_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
+    "oxa_paged_decode_balanced_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "oxa_paged_decode_noalloc": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _P, _P, _I, _P,
                                       _I, _F, _I, _P, _P, _P]),
     "oxa_ragged_prefill": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
@@ -276,6 +277,16 @@ def oxa_paged_append(k_in, v_in, batch_indices, positions, k_pages, v_pages, pag
 def oxa_paged_decode_workspace_bytes(batch, num_qo_heads, num_partitions, head_dim=HEAD_DIM) -> int:
     return int(lib().oxa_paged_decode_workspace_bytes(batch, num_qo_heads, head_dim,
                                                       num_partitions))
+
+
+def oxa_paged_decode_balanced_workspace_bytes(batch, num_qo_heads, num_partitions,
+                                              head_dim=HEAD_DIM) -> int:
+    """Workspace bytes of the load-balanced decode mode (0 if the shape has none).
+
+    Its merge counters must be zero before the first call with a workspace;
+    every call leaves them zero (a zero-filled workspace can be reused)."""
+    return int(lib().oxa_paged_decode_balanced_workspace_bytes(batch, num_qo_heads, head_dim,
+                                                              num_partitions))
 
 
 def oxa_paged_decode(q, k_pages, v_pages, page_indptr, page_indices, seq_lens, o, *,

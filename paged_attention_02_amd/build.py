@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liboxa.so")
-SOURCES = ["decode.hip", "append.hip", "prefill.hip", "merge.hip", "rope.hip", "oxa_host.cpp"]
+SOURCES = ["decode.hip", "decode_balanced.hip", "append.hip", "prefill.hip", "merge.hip", "rope.hip", "oxa_host.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-FP32 VALU forms are kept out of the generated code on purpose.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -120,6 +120,19 @@ __device__ __forceinline__ float pair_max32(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// max and sum of v over the lane pair (l, l ^ 16)
+__device__ __forceinline__ float pair_max16(float v) {
+  const uint32_t b = __float_as_uint(v);
+  auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum16(float v) {
+  const uint32_t b = __float_as_uint(v);
+  auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float pair_sum32(float v) {
   const uint32_t b = __float_as_uint(v);
   auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);

@@ -23,6 +23,22 @@ struct DecodeLaunch {
   float sm_scale;
 };
 hipError_t launch_paged_decode(const DecodeLaunch& a, hipStream_t stream);
+// Load-balanced decode (equal page ranges per work-group, pieces merged by a
+// second kernel), used for calls with the workspace for it.  Workspace after
+// the partition states: the unit page starts (int32 [units + 1]), then the
+// piece states: o f32 [G + units][hq][128] and lse f32 [G + units][hq].
+constexpr int kBalancedMaxUnits = 2048;   // batch * partitions
+constexpr int kBalancedMaxRanges = 512;   // G, the page ranges
+struct BalancedLayout {
+  int32_t* meta;
+  float* piece_o;
+  float* piece_lse;
+};
+hipError_t launch_paged_decode_balanced(const DecodeLaunch& a, const BalancedLayout& ws, int G,
+                                        hipStream_t stream);
+// Compute units of the current device (queried once per device).
+hipError_t device_cu_count(int* cus);
+
 // Bytes of the per-device static scratch behind the allocation-free decode,
 // and its device address on the current device (resolved once per device).
 constexpr size_t kDecodeScratchBytes = (size_t)8 << 20;

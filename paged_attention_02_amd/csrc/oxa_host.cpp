@@ -8,6 +8,7 @@
 // are typed status codes; enqueue neither tunes nor falls back silently.
 // Every check below runs on the host before the first HIP call, so a rejected
 // call touches no device state.
+#include <algorithm>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -109,6 +110,26 @@ uint64_t prefill_tiles(int32_t hq, int32_t hkv, int32_t max_qo_len) {
   return ((uint64_t)max_qo_len + bm - 1) / bm;
 }
 
+
+// Split-K partition states of a decode call (o_part then lse_part, f32);
+// 0 for a call without partitions.
+uint64_t decode_state_bytes(int32_t batch, int32_t hq, int32_t partitions) {
+  if (partitions <= 1) return 0;
+  const uint64_t rows = (uint64_t)batch * hq * partitions;
+  return rows * OXA_HEAD_DIM * 4 + rows * 4;
+}
+
+uint64_t align256(uint64_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace of the load-balanced decode: the partition states, the unit page
+// starts (int32 [units + 1]) and the piece states of at most
+// kBalancedMaxRanges + units pieces (o f32 [..][hq][128], then lse f32 [..][hq]).
+uint64_t decode_balanced_bytes(int32_t batch, int32_t hq, int32_t partitions) {
+  const uint64_t units = (uint64_t)batch * partitions;
+  const uint64_t slots = (uint64_t)oxa::kBalancedMaxRanges + units;
+  return align256(decode_state_bytes(batch, hq, partitions)) + align256((units + 1) * 4) +
+         align256(slots * hq * OXA_HEAD_DIM * 4) + slots * hq * 4;
+}
 
 // Checks shared by both RoPE entry points; fills everything but the table.
 oxa_status rope_setup(const uint16_t* q_in, uint16_t* q_out, int32_t num_qo_heads,
@@ -336,9 +357,20 @@ oxa_status oxa_paged_append(hipStream_t stream, const uint16_t* k_in, const uint
 
 size_t oxa_paged_decode_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t head_dim,
                                         int32_t num_partitions) {
-  if (batch < 1 || num_qo_heads < 1 || head_dim != OXA_HEAD_DIM || num_partitions <= 1) return 0;
-  const uint64_t rows = (uint64_t)batch * num_qo_heads * num_partitions;
-  return (size_t)(rows * OXA_HEAD_DIM * 4 + rows * 4);
+  if (batch < 1 || num_qo_heads < 1 || head_dim != OXA_HEAD_DIM || num_partitions < 1 ||
+      num_partitions > 1024)
+    return 0;
+  return (size_t)decode_state_bytes(batch, num_qo_heads, num_partitions);
+}
+
+size_t oxa_paged_decode_balanced_workspace_bytes(int32_t batch, int32_t num_qo_heads,
+                                                 int32_t head_dim, int32_t num_partitions) {
+  if (batch < 1 || num_qo_heads < 1 || head_dim != OXA_HEAD_DIM || num_partitions < 1 ||
+      num_partitions > 1024)
+    return 0;
+  const uint64_t units = (uint64_t)batch * num_partitions;
+  if (units > (uint64_t)oxa::kBalancedMaxUnits) return 0;
+  return (size_t)decode_balanced_bytes(batch, num_qo_heads, num_partitions);
 }
 
 }  // extern "C"
@@ -370,12 +402,31 @@ oxa_status paged_decode_impl(hipStream_t stream, const uint16_t* q, int32_t batc
       !aligned(workspace, 16) || !aligned(lse, 4) || !aligned(status, 4) ||
       !aligned(page_indptr, 4) || !aligned(page_indices, 4) || !aligned(seq_lens, 4))
     return OXA_ERR_ALIGN;
-  const size_t need = oxa_paged_decode_workspace_bytes(batch, num_qo_heads, head_dim,
-                                                       num_partitions);
+  const size_t need = (size_t)decode_state_bytes(batch, num_qo_heads, num_partitions);
   if (use_scratch) {
     if (need > oxa::kDecodeScratchBytes) return OXA_ERR_SCRATCH_LIMIT;
   } else if (need > 0 && (workspace == nullptr || workspace_bytes < need)) {
     return OXA_ERR_WORKSPACE;
+  }
+  // The load-balanced path: with a workspace of the full size the query
+  // returns, at most kBalancedMaxUnits units, and enough pages for every
+  // range to get several (a small call is faster in the direct kernel).
+  const uint64_t units = (uint64_t)batch * num_partitions;
+  int cus = 0;
+  int G = 0;
+  size_t used = need;
+  if (!use_scratch && workspace != nullptr && units <= (uint64_t)oxa::kBalancedMaxUnits &&
+      workspace_bytes >= decode_balanced_bytes(batch, num_qo_heads, num_partitions)) {
+    if (oxa::device_cu_count(&cus) != hipSuccess) return OXA_ERR_LAUNCH;
+    // one range per compute unit, each of 4 pages or more of the largest
+    // possible total (the real total, from seq_lens, is known on the device)
+    const uint64_t max_pages = (uint64_t)batch * ((max_seq_len + OXA_PAGE_SIZE - 1) / OXA_PAGE_SIZE);
+    const int64_t g = std::min<int64_t>(std::min<int64_t>(oxa::kBalancedMaxRanges, cus),
+                                        (int64_t)(max_pages / 4));
+    if (max_pages >= 64 && g >= 1) {
+      G = (int)g;
+      used = (size_t)decode_balanced_bytes(batch, num_qo_heads, num_partitions);
+    }
   }
 
   const uint64_t B = (uint64_t)batch;
@@ -389,7 +440,7 @@ oxa_status paged_decode_impl(hipStream_t stream, const uint16_t* q, int32_t batc
   const Region outs[] = {{o, B * num_qo_heads * kRowBytes},
                          {lse, lse ? B * num_qo_heads * 4 : 0},
                          {status, status ? B * 4 : 0},
-                         {use_scratch ? nullptr : workspace, need}};
+                         {use_scratch ? nullptr : workspace, used}};
   if (any_alias(outs, 4, ins, 6)) return OXA_ERR_ALIAS;
   if (use_scratch && need > 0) {
     // the library's own array: it overlaps nothing the caller owns
@@ -422,6 +473,18 @@ oxa_status paged_decode_impl(hipStream_t stream, const uint16_t* q, int32_t batc
   const int32_t max_pages = (max_seq_len + OXA_PAGE_SIZE - 1) / OXA_PAGE_SIZE;
   a.chunk_pages = (max_pages + num_partitions - 1) / num_partitions;
   a.sm_scale = sm_scale;
+  if (G > 0) {
+    unsigned char* base = static_cast<unsigned char*>(workspace);
+    const uint64_t slots = (uint64_t)oxa::kBalancedMaxRanges + units;
+    const uint64_t meta_off = align256(need);
+    const uint64_t po_off = meta_off + align256((units + 1) * 4);
+    const uint64_t pl_off = po_off + align256(slots * num_qo_heads * OXA_HEAD_DIM * 4);
+    oxa::BalancedLayout ws;
+    ws.meta = reinterpret_cast<int32_t*>(base + meta_off);
+    ws.piece_o = reinterpret_cast<float*>(base + po_off);
+    ws.piece_lse = reinterpret_cast<float*>(base + pl_off);
+    return launch_status(oxa::launch_paged_decode_balanced(a, ws, G, stream));
+  }
   return launch_status(oxa::launch_paged_decode(a, stream));
 }
 

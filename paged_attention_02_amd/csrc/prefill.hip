@@ -576,7 +576,7 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
 // Compute units of the current device, queried once per device: the
 // attribute query walks the runtime's device properties and costs more host
 // time than a short prefill takes on the GPU.
-static hipError_t device_cu_count(int* cus) {
+hipError_t device_cu_count(int* cus) {
   constexpr int kMaxDevices = 64;
   static std::atomic<int> cached[kMaxDevices];
   int dev = 0;

@@ -155,6 +155,13 @@ def decode_gqa4_batch(poison=False, layout="NHD", num_partitions=1, batch=32,
                        num_partitions=num_partitions)
 
 
+def decode_skewed(poison=False, layout="NHD") -> DecodeCase:
+    """Skewed batch-32 GQA4 decode: one 32768-token sequence and 31 of 1024
+    (32 q / 8 kv heads), the case load balancing is for."""
+    return decode_case(1006, batch=32, num_qo_heads=32, num_kv_heads=8,
+                       seq_lens=[32768] + [1024] * 31, layout=layout, poison=poison)
+
+
 def decode_mqa_long(poison=False, layout="NHD", seq_len=32768, batch=8,
                     num_partitions=16) -> DecodeCase:
     """Long MQA decode: batch 8, 32 q heads / 1 kv head, seq_len 32768, 16 KV partitions."""
