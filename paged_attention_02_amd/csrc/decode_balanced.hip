@@ -274,31 +274,6 @@ __global__ __launch_bounds__(kNW * 64) void balanced_decode_kernel(BalParams p) 
       }
     }
   };
-  // pair pr of a piece's page-id window (pages 2*pr, 2*pr + 1 of the window;
-  // window base w0 within the piece, n_tok tokens in the piece)
-  auto issue = [&](int pr, int w0, int wpages, int n_tok, Rows& r) {
-#pragma unroll
-    for (int pg = 0; pg < 2; ++pg) {
-      const int sb = min(2 * pr + pg, wpages - 1);
-      const int pid = __builtin_amdgcn_readfirstlane(max(pids[sb], 0));
-      const int last = 2 * pr + pg < wpages ? min(kPage, n_tok - (w0 + sb) * kPage) - 1 : 0;
-      const unsigned char* ka = kb + pid * page_bytes;
-      const unsigned char* va = vb + pid * page_bytes;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const uint32_t off = (uint32_t)(min(4 * q4 + gq, last) * row_bytes) + lane_chunk;
-        const u32x4_t* kp4 = reinterpret_cast<const u32x4_t*>(ka + off);
-        const u32x4_t* vp4 = reinterpret_cast<const u32x4_t*>(va + off);
-        if constexpr (NT) {
-          r.k[pg][q4] = __builtin_nontemporal_load(kp4);
-          r.v[pg][q4] = __builtin_nontemporal_load(vp4);
-        } else {
-          r.k[pg][q4] = *kp4;
-          r.v[pg][q4] = *vp4;
-        }
-      }
-    }
-  };
   auto stage = [&](const Rows& r) {
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg)
@@ -450,144 +425,23 @@ __global__ __launch_bounds__(kNW * 64) void balanced_decode_kernel(BalParams p) 
     }
   };
 
-  if constexpr (INDEP) {
-    // ---- one set per wave: the waves run through the range independently.
-    // Page descriptors of a window of the range (id and unit | valid tokens
-    // << 16), staged together; each wave walks page pairs that never cross a
-    // unit or window end, prefetching the next pair's rows across piece ends,
-    // and writes a finished piece's states from its registers.
-    int* pinfo = reinterpret_cast<int*>(smem + kLdsPinfo);
-    for (int w0 = s0; w0 < s1; w0 += kPidWin) {
-      const int wend = min(s1, w0 + kPidWin);
-      __syncthreads();  // the previous window's descriptors are free
-      for (int i = tid; i < wend - w0; i += kNW * 64) {
-        const int f = w0 + i;
-        int lo = 0, hi = p.units - 1;  // last unit starting at or before f
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (ustart[mid] <= f) lo = mid; else hi = mid - 1;
-        }
-        const int uu = lo;  // unit_pages > 0 for the unit holding f
-        const int pid = p.page_indices[uptr[uu] + (f - ustart[uu])];
-        pids[i] = (pid >= 0 && pid < p.num_pages) ? pid : -1;
-        pinfo[i] = uu | ((f == ustart[uu + 1] - 1 ? utail[uu] : kPage) << 16);
-      }
-      __syncthreads();
-      if (!busy) continue;
-      // pair starting at window page i: its length (1 or 2) and unit
-      auto unit_at = [&](int i) { return pinfo[i] & 0xffff; };
-      auto pair_len = [&](int i) {
-        return (i + 1 < wend - w0 && unit_at(i + 1) == unit_at(i)) ? 2 : 1;
-      };
-      auto issue_at = [&](int i, int len, Rows& r) {
-        int pid2[2] = {pids[i], pids[i + len - 1]};
-        int last2[2] = {(pinfo[i] >> 16) - 1, len == 2 ? (pinfo[i + 1] >> 16) - 1 : 0};
-        issue_pages(pid2, last2, r);
-      };
-      // the unit whose piece is open at the window start (state carried over
-      // from the previous window) is known from the first page
-      int i = 0;
-      int len = pair_len(0);
-      int ucur = unit_at(0);
-      Rows r;
-      issue_at(0, len, r);
-      const bool carried = w0 > s0 && ustart[ucur] < w0;
-      if (!carried) start_piece(ucur);
-      while (true) {
-        const int nxt = i + len;
-        const int nlen = nxt < wend - w0 ? pair_len(nxt) : 0;
-        stage(r);
-        if (nlen > 0) issue_at(nxt, nlen, r);
-        compute(pinfo[i] >> 16, len == 2 ? pinfo[i + 1] >> 16 : 0);
-        const int unxt = nlen > 0 ? unit_at(nxt) : -1;
-        if (unxt != ucur) {
-          // the piece of ucur ends here unless it goes on past this window
-          const int pe = min(s1, ustart[ucur + 1]);
-          if (w0 + nxt >= pe) finish_piece_wave(ucur);
-          if (unxt < 0) break;
-          ucur = unxt;
-          start_piece(ucur);
-        }
-        i = nxt;
-        len = nlen;
-      }
-    }
-  } else {
-  // ---- the pieces of this range --------------------------------------------
-  int u = 0;
-  {
-    // last unit starting at or before s0, then skip empty ones
-    int lo = 0, hi = p.units - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (ustart[mid] <= s0) lo = mid; else hi = mid - 1;
-    }
-    u = lo;
-    while (u < p.units && ustart[u + 1] <= s0) ++u;
-  }
-  for (; s0 < s1 && u < p.units && ustart[u] < s1; ++u) {
+  // Several waves per set: merge their states of the finished piece of unit
+  // u through LDS and write them.  Every wave of the work-group calls it at
+  // the same piece end.  LDS (the row slices, free by then): per wave-state
+  // slot ls the column max and sum [16] and the accumulator laid out
+  // [d][e][g][c] for lane (c, g)'s acc[d][e], so the 64 lanes of a store write
+  // 64 consecutive words.
+  auto finish_piece_shared = [&](int u) {
     const int us = ustart[u], ue = ustart[u + 1];
-    if (ue == us) continue;
     const int pa = max(s0, us), pb = min(s1, ue);
+    const bool whole = pa == us && pb == ue;
+    const int slot = pa == s0 ? w : p.G + u;
     const int b = u / p.num_partitions;
     const int part = u - b * p.num_partitions;
-    const int L = p.seq_lens[b];
-    const int seq_page0 = part * p.chunk_pages + (pa - us);  // first page of the piece
-    const int npg = pb - pa;
-    const int n_tok = min(npg * kPage, L - seq_page0 * kPage);
-    const int entry0 = p.page_indptr[b] + seq_page0;
-
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      if (col_ok[i]) {
-        const int head = kvh * p.group + (tile0 + i) * kHT + col;
-        const uint16_t* qp = p.q + ((int64_t)b * p.hq + head) * kHeadDim + 8 * gq;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qf[i][kk] = ldg16(qp + 32 * kk);
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qf[i][kk] = u32x4_t{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int d = 0; d < 8; ++d) acc[i][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      m[i] = -INFINITY;
-      lsum[i] = 0.f;
-    }
-
-    for (int w0 = 0; w0 < npg; w0 += kPidWin) {
-      const int wpages = min(kPidWin, npg - w0);
-      __syncthreads();  // the previous window's page ids, or the previous piece's LDS, are free
-      for (int i = tid; i < wpages; i += kNW * 64) {
-        const int pid = p.page_indices[entry0 + w0 + i];
-        pids[i] = (pid >= 0 && pid < p.num_pages) ? pid : -1;
-      }
-      __syncthreads();
-      const int npr = (wpages + 1) / 2;
-      auto valid_of = [&](int sb) {
-        return sb < wpages ? min(kPage, n_tok - (w0 + sb) * kPage) : 0;
-      };
-      if (busy) {
-        Rows r;
-        int pr = tgi;
-        if (pr < npr) {
-          issue(pr, w0, wpages, n_tok, r);
-          stage(r);
-        }
-        while (pr < npr) {
-          const int nxt = pr + tgn;
-          if (nxt < npr) issue(nxt, w0, wpages, n_tok, r);
-          compute(valid_of(2 * pr), valid_of(2 * pr + 1));
-          if (nxt < npr) stage(r);
-          pr = nxt;
-        }
-      }
-    }
-    __syncthreads();  // every wave is done with its slice before the epilogue reuses LDS
-
-    // ---- piece epilogue: merge the waves of each set, write the states.
     float* red_m = reinterpret_cast<float*>(smem);  // [kSlots][16]
     float* red_l = red_m + kSlots * kHT;            // [kSlots][16]
-    float* red_o = red_l + kSlots * kHT;            // [kSlots][128][16]
+    float* red_o = red_l + kSlots * kHT;            // [kSlots][8][4][4][16]
+    __syncthreads();  // every wave is done with its row slice
     if (busy) {
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
@@ -601,14 +455,11 @@ __global__ __launch_bounds__(kNW * 64) void balanced_decode_kernel(BalParams p) 
 #pragma unroll
         for (int d = 0; d < 8; ++d)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            red_o[(ls * kHeadDim + 16 * d + 4 * gq + e) * kHT + col] = acc[i][d][e];
+          for (int e = 0; e < 4; ++e) red_o[((ls * 8 + d) * 4 + e) * 64 + lane] = acc[i][d][e];
       }
     }
     __syncthreads();
     // thread (k, i, c, dc): set k, its stream i, q head c, dims 8*dc .. +8
-    const bool whole = pa == us && pb == ue;
-    const int slot = pa == s0 ? w : p.G + u;  // piece slot (split units only)
     for (int item = tid; item < nsets * NS * kHT * 16; item += kNW * 64) {
       const int k = item / (NS * kHT * 16);
       const int i = (item / (kHT * 16)) % NS;
@@ -627,12 +478,14 @@ __global__ __launch_bounds__(kNW * 64) void balanced_decode_kernel(BalParams p) 
       for (int t = 0; t < tgn; ++t) {
         const float f = fast_exp2(red_m[(lbase + t) * kHT + c] - Muse);
         Lt += red_l[(lbase + t) * kHT + c] * f;
+        // dims 8*dc + j: d = dc / 2, g = 2 * (dc % 2) + j / 4, e = j % 4
+        const float* ro = red_o + (((lbase + t) * 8 + (dc >> 1)) * 4) * 64 + (2 * (dc & 1)) * 16 + c;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) val[e] += red_o[((lbase + t) * kHeadDim + 8 * dc + e) * kHT + c] * f;
+        for (int j = 0; j < 8; ++j) val[j] += ro[(j & 3) * 64 + (j >> 2) * 16] * f;
       }
       const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) val[e] *= inv;
+      for (int j = 0; j < 8; ++j) val[j] *= inv;
       const float lse_val = Lt > 0.f ? (M + __log2f(Lt)) * kLn2 : -INFINITY;
       const int head = kvhk * p.group + tile * kHT + c;
       const int64_t hrow = (int64_t)b * p.hq + head;
@@ -658,9 +511,85 @@ __global__ __launch_bounds__(kNW * 64) void balanced_decode_kernel(BalParams p) 
         if (dc == 0) *ldst = lse_val;
       }
     }
-  }
+    __syncthreads();  // the slices are free for the next pair's rows
+  };
 
-  }  // INDEP
+  // ---- the pages of this range, a window of descriptors at a time.
+  // Descriptors (page id, and unit | valid tokens << 16) of up to kPidWin
+  // pages are staged together.  The range's pieces (one per unit it touches)
+  // are walked in order by every wave; within a piece the page pairs
+  // (2k, 2k+1 from the piece's start in the window) go to the set's waves in
+  // turn (pair k to wave tgi = k mod tgn).  A wave's next pair is prefetched
+  // whatever piece it lies in, so piece ends do not drain the load pipeline.
+  int* pinfo = reinterpret_cast<int*>(smem + kLdsPinfo);
+  for (int w0 = s0; w0 < s1; w0 += kPidWin) {
+    const int wend = min(s1, w0 + kPidWin);
+    const int wlen = wend - w0;
+    __syncthreads();  // the previous window's descriptors are free
+    for (int i = tid; i < wlen; i += kNW * 64) {
+      const int f = w0 + i;
+      int lo = 0, hi = p.units - 1;  // last unit starting at or before f
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (ustart[mid] <= f) lo = mid; else hi = mid - 1;
+      }
+      const int uu = lo;  // unit_pages > 0 for the unit holding f
+      const int pid = p.page_indices[uptr[uu] + (f - ustart[uu])];
+      pids[i] = (pid >= 0 && pid < p.num_pages) ? pid : -1;
+      pinfo[i] = uu | ((f == ustart[uu + 1] - 1 ? utail[uu] : kPage) << 16);
+    }
+    __syncthreads();
+    auto unit_at = [&](int i) { return pinfo[i] & 0xffff; };
+    // window-local end of the piece that starts at window page i
+    auto piece_end = [&](int i) { return min(wend, ustart[unit_at(i) + 1]) - w0; };
+    // pair k of the piece starting at pa (its end pe), or else pair tgi of a
+    // later piece; false past the window
+    auto find = [&](int& pa, int& k, int& pe) {
+      while (pa < wlen) {
+        pe = piece_end(pa);
+        if (2 * k < pe - pa) return true;
+        pa = pe;
+        k = tgi;
+      }
+      return false;
+    };
+    auto issue_item = [&](int pa, int k, int pe, Rows& r) {
+      const int i = pa + 2 * k;
+      const int len = i + 1 < pe ? 2 : 1;
+      int pid2[2] = {pids[i], pids[i + len - 1]};
+      int last2[2] = {(pinfo[i] >> 16) - 1, len == 2 ? (pinfo[i + 1] >> 16) - 1 : 0};
+      issue_pages(pid2, last2, r);
+    };
+    Rows r;
+    int cpa = 0, ck = tgi, cpe = 0;  // this wave's current pair
+    bool have = busy && find(cpa, ck, cpe);
+    if (have) issue_item(cpa, ck, cpe, r);
+    for (int pa = 0; pa < wlen;) {
+      const int u = unit_at(pa);
+      const int pe = piece_end(pa);
+      // a piece already open at the window start goes on with its state
+      if (!(pa == 0 && w0 > s0 && ustart[u] < w0)) start_piece(u);
+      while (have && cpa == pa) {
+        int npa = cpa, nk = ck + tgn, npe = 0;
+        const bool hn = find(npa, nk, npe);
+        stage(r);
+        if (hn) issue_item(npa, nk, npe, r);
+        const int i = cpa + 2 * ck;
+        compute(pinfo[i] >> 16, i + 1 < cpe ? pinfo[i + 1] >> 16 : 0);
+        cpa = npa;
+        ck = nk;
+        cpe = npe;
+        have = hn;
+      }
+      if (w0 + pe == min(s1, ustart[u + 1])) {  // the piece ends in this window
+        if constexpr (INDEP)
+          finish_piece_wave(u);
+        else
+          finish_piece_shared(u);
+      }
+      pa = pe;
+    }
+  }
 
   // ---- per-sequence status: work-group w (set group 0) checks the
   // sequences b = w, w + G, ... after its attention work
