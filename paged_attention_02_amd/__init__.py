@@ -19,7 +19,8 @@ import os
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboxa.so")
+# the built library; OXA_LIBRARY names another build of it (a sanitized host layer, say)
+LIB_PATH = os.environ.get("OXA_LIBRARY") or os.path.join(_HERE, "liboxa.so")
 
 OXA_OK = 0
 OXA_ERR_NULL = 1

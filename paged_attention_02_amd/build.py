@@ -46,5 +46,31 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     return LIB
 
 
+HOST_SANITIZED = os.path.join(BUILD, "liboxa_host_sanitized.so")
+
+
+def build_host_sanitized(jobs: int = 4) -> str:
+    """liboxa with its host layer (argument checks, workspace layout, launch
+    set-up) built under AddressSanitizer and UndefinedBehaviorSanitizer, host
+    pass only; the kernels are the regular objects.  For CPU tests of the host
+    layer: load it with the ASan runtime preloaded (see the host sanitizer test)."""
+    objs = []
+    missing = [s for s in SOURCES if s != "oxa_host.cpp" and
+               not os.path.exists(os.path.join(BUILD, s + ".o"))]
+    if missing:
+        build(jobs=jobs)
+    for src in SOURCES:
+        if src != "oxa_host.cpp":
+            objs.append(os.path.join(BUILD, src + ".o"))
+    obj = os.path.join(BUILD, "oxa_host_sanitized.o")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+           "-g"]
+    _run([HIPCC, *FLAGS, *san, "-c", os.path.join(CSRC, "oxa_host.cpp"), "-o", obj])
+    # the sanitizer runtime is not linked in: the process preloads it
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", obj, *objs, "-o", HOST_SANITIZED])
+    return HOST_SANITIZED
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

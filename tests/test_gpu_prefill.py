@@ -198,6 +198,20 @@ def _sample_rows(qo_indptr, per_seq, rng):
     return np.array(rows)
 
 
+def _full_tile_rows(qo_indptr, tile=64):
+    """Every row of whole query tiles (64 rows x the 4 q heads of a kv head in
+    the GQA4 shapes): the last two tiles of each sequence (the longest causal
+    level) and a tile pair in its middle, aligned to the tile grid."""
+    rows = []
+    for b in range(len(qo_indptr) - 1):
+        s, e = int(qo_indptr[b]), int(qo_indptr[b + 1])
+        n = e - s
+        mid = s + (n // 2 // tile) * tile
+        pick = set(range(max(s, e - 2 * tile), e)) | set(range(mid, min(e, mid + 2 * tile)))
+        rows += sorted(pick)
+    return np.array(rows)
+
+
 def test_ragged_prefill_full_size_sampled():
     # lengths {512, 1024, 2048, 4096}, 32 q / 8 kv heads, causal
     case = W.ragged_gqa4_prefill()
@@ -209,6 +223,12 @@ def test_ragged_prefill_full_size_sampled():
                               case.sm_scale, True, rows=rows)
     assert_attention_close(got["o"][rows], o[rows], "ragged full sampled")
     assert_lse_close(got["lse"][rows], lse[rows])
+    # whole query tiles, all 32 heads: the last 128 rows and a mid pair per sequence
+    tiles = _full_tile_rows(case.qo_indptr)
+    o, lse = A.ragged_prefill(case.q, case.k, case.v, case.qo_indptr, case.kv_indptr,
+                              case.sm_scale, True, rows=tiles)
+    assert_attention_close(got["o"][tiles], o[tiles], "ragged full tiles")
+    assert_lse_close(got["lse"][tiles], lse[tiles])
 
 
 def test_rope_append_then_paged_prefill_full_size_sampled():
@@ -228,11 +248,12 @@ def test_rope_append_then_paged_prefill_full_size_sampled():
                                    rope_theta=case.rope_theta)
     assert rc == oxa.OXA_OK
     o = torch.zeros_like(q_in)
+    lse = torch.empty(q_in.shape[0], q_in.shape[1], dtype=torch.float32, device="cuda")
     st2 = torch.full((2,), -1, dtype=torch.int32, device="cuda")
     rc = oxa.oxa_paged_prefill(q_rot, dev(case.qo_indptr), kp, vp, indptr, ids,
                                dev(kv.seq_lens), o, max_qo_len=16384, max_seq_len=16384,
                                sm_scale=case.sm_scale, layout=kv.layout, num_kv_heads=8,
-                               causal=True, status=st2)
+                               causal=True, lse=lse, status=st2)
     assert rc == oxa.OXA_OK
     torch.cuda.synchronize()
     assert host(status).tolist() == [0, -1] and host(st2).tolist() == [0, 0]
@@ -244,4 +265,14 @@ def test_rope_append_then_paged_prefill_full_size_sampled():
     rows = _sample_rows(case.qo_indptr, 12, np.random.default_rng(1))
     o_ref, _ = A.paged_prefill(q_ref, case.qo_indptr, k_ref, v_ref, kv.layout, kv.page_indptr,
                                kv.page_indices, kv.seq_lens, case.sm_scale, True, rows=rows)
-    assert_attention_close(host_bits(o)[rows], o_ref[rows], "paged prefill full sampled")
+    got_o, got_lse = host_bits(o), host(lse)
+    assert_attention_close(got_o[rows], o_ref[rows], "paged prefill full sampled")
+    # whole query tiles, all 32 heads: the last 128 rows of each 16384-row
+    # sequence (the longest causal level) and a tile pair in its middle
+    tiles = _full_tile_rows(case.qo_indptr)
+    note(f"paged prefill full tiles: {len(tiles)} rows x 32 heads against the oracle")
+    o_ref, lse_ref = A.paged_prefill(q_ref, case.qo_indptr, k_ref, v_ref, kv.layout,
+                                     kv.page_indptr, kv.page_indices, kv.seq_lens, case.sm_scale,
+                                     True, rows=tiles)
+    assert_attention_close(got_o[tiles], o_ref[tiles], "paged prefill full tiles")
+    assert_lse_close(got_lse[tiles], lse_ref[tiles])
