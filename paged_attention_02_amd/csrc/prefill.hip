@@ -372,6 +372,28 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
       voff[d][a] = kTileBytes + swz_off(r, c) + 8 * (i16 & 1);
     }
 
+  // Loads of a whole tile (every key exists): this lane's two 16-byte pieces
+  // are fixed offsets from the tile's first key row (ragged) or from the page
+  // that holds the wave's 8 rows (paged: rows 8*wave .. +7 lie in page
+  // wave / 2 of the tile's 4), so a tile costs one page-id read per wave and
+  // one 64-bit add per load.  The partial last tile takes issue_tile.
+  uint32_t ld_off[kLoadIters];
+#pragma unroll
+  for (int u = 0; u < kLoadIters; ++u) {
+    const int row = wave * (4 * kLoadIters) + 4 * u + (lane >> 4);
+    const int sw = ((row & 3) << 2) | ((row >> 2) & 3);
+    const int chunk = (lane & 15) ^ sw;
+    const int slot = row & (kPage - 1);
+    if (!PAGED)
+      ld_off[u] = (uint32_t)((row * p.hkv + kvh) * kHeadDim + chunk * 8);
+    else if (LAYOUT == 0)
+      ld_off[u] = (uint32_t)((slot * p.hkv + kvh) * kHeadDim + chunk * 8);
+    else
+      ld_off[u] = (uint32_t)((kvh * kPage + slot) * kHeadDim + chunk * 8);
+  }
+  const int64_t page_elems = (int64_t)kPage * p.hkv * kHeadDim;
+  static_assert(kLoadIters * 4 * kNW == kBN && kBN == 4 * kPage, "8 rows per wave, 4 pages per tile");
+
   // Paged K/V: the sequence's page ids for keys [0, kv_end), staged per window
   // of kPidWin pages (invalid ids become -1).
   const int npages_need = (kv_end + kPage - 1) / kPage;
@@ -388,12 +410,31 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
   };
   constexpr int kTilesPerWin = kPidWin * kPage / kBN;
   int wbase = kt0 / kTilesPerWin * kPidWin;  // the page-id window of tile kt0
+  auto issue = [&](int kt, unsigned char* ks, unsigned char* vs) {
+    if (kt * kBN + kBN > si.klen) {
+      issue_tile<PAGED, LAYOUT>(p, si, kvh, kt, wave, lane, pids, wbase, ks, vs);
+      return;
+    }
+    int64_t base;
+    if (PAGED) {
+      // an invalid page reads page 0 (the sequence's status says so)
+      const int pid = __builtin_amdgcn_readfirstlane(max(pids[kt * 4 + (wave >> 1) - wbase], 0));
+      base = (int64_t)pid * page_elems;
+    } else {
+      base = (int64_t)(si.kbase + kt * kBN) * p.hkv * kHeadDim;
+    }
+#pragma unroll
+    for (int u = 0; u < kLoadIters; ++u) {
+      const int lds_off = (wave * (4 * kLoadIters) + 4 * u) * 256;
+      dma16(p.k + base + ld_off[u], lds_addr(ks + lds_off));
+      dma16(p.v + base + ld_off[u], lds_addr(vs + lds_off));
+    }
+  };
   if (PAGED) stage_pids(wbase);
   __syncthreads();
 
   // Tile kt0 goes to buffer 0, kt0 + 1 to buffer 1, and so on.
-  if (kt1 > kt0)
-    issue_tile<PAGED, LAYOUT>(p, si, kvh, kt0, wave, lane, pids, wbase, smem, smem + kTileBytes);
+  if (kt1 > kt0) issue(kt0, smem, smem + kTileBytes);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
@@ -412,7 +453,7 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
     }
     if (kt + 1 < kt1) {  // tile kt+1 streams into the other buffer meanwhile
       unsigned char* kn = smem + (1 - BUF) * 2 * kTileBytes;
-      issue_tile<PAGED, LAYOUT>(p, si, kvh, kt + 1, wave, lane, pids, wbase, kn, kn + kTileBytes);
+      issue(kt + 1, kn, kn + kTileBytes);
     }
 
     const int key0 = kt * kBN;

@@ -158,7 +158,7 @@ def decode_gqa4_batch(poison=False, layout="NHD", num_partitions=1, batch=32,
 def decode_skewed(poison=False, layout="NHD") -> DecodeCase:
     """Skewed batch-32 GQA4 decode: one 32768-token sequence and 31 of 1024
     (32 q / 8 kv heads), the case load balancing is for."""
-    return decode_case(1006, batch=32, num_qo_heads=32, num_kv_heads=8,
+    return decode_case(1010, batch=32, num_qo_heads=32, num_kv_heads=8,
                        seq_lens=[32768] + [1024] * 31, layout=layout, poison=poison)
 
 
