@@ -92,12 +92,6 @@ __host__ __device__ __forceinline__ uint16_t bf16_from_double_rne(double x) {
   return (uint16_t)(sign | bits);
 }
 
-// acc + lo + hi of a packed bf16 pair, in f32 (one v_dot2 against (1, 1))
-__device__ __forceinline__ float dot2_bf16_sum(uint32_t pair, float acc) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair),
-                                         __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
-}
-
 // 2^x on the transcendental unit (v_exp_f32; results below 2^-126 flush to
 // zero, which a softmax weight may do)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
