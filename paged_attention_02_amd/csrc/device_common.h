@@ -172,6 +172,19 @@ __device__ __forceinline__ uint32_t bf16_rne(double y) {
   return bf16_from_double_rne(y);
 }
 
+// bf16 bits of f32 `r` rounded to nearest even, and whether that equals the
+// rounding of every value within `e` of r: r must lie farther than e from the
+// midpoint of its bf16 cell (r - mid is exact: same sign and exponent), and e
+// must be under a quarter of r's bf16 ulp (below a power of two the cell
+// underneath is half as wide).  Zero, subnormal and non-finite r never pass.
+__device__ __forceinline__ uint32_t bf16_rne_checked(float r, float e, bool& ok) {
+  const uint32_t u = __float_as_uint(r);
+  const float mid = __uint_as_float((u & 0xffff0000u) | 0x8000u);
+  const float binade = __uint_as_float(u & 0x7f800000u);  // 2^exponent(r)
+  ok = ok && (fabsf(r - mid) > e) && (e * 512.f < binade);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
 // Rotate one 8-pair chunk: x1 = dims [8f, 8f+8), x2 = dims [64+8f, 64+8f+8).
 __device__ __forceinline__ void rotate_chunk(u32x4_t w1, u32x4_t w2, const double* c,
                                              const double* s, u32x4_t* out1, u32x4_t* out2) {
@@ -184,6 +197,47 @@ __device__ __forceinline__ void rotate_chunk(u32x4_t w1, u32x4_t w2, const doubl
     const double a = x1[i], bb = x2[i];
     y1[i] = bf16_rne(a * c[i] - bb * s[i]);
     y2[i] = bf16_rne(bb * c[i] + a * s[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    (*out1)[i] = y1[2 * i] | (y1[2 * i + 1] << 16);
+    (*out2)[i] = y2[2 * i] | (y2[2 * i + 1] << 16);
+  }
+}
+
+// rotate_chunk with the same results from f32 arithmetic where that is provably
+// enough: y1 = x1 cos - x2 sin, y2 = x2 cos + x1 sin, each rounded once to bf16
+// as the double-precision expression would be.  cs: the double (cos, sin) of
+// the 8 frequencies (read only on the rare double-precision path, so it may
+// stay in LDS); cf, sf: the same rounded to f32.
+//
+// The rotation is first formed in f32: with bf16 (hence exact f32) inputs and
+// |cos|, |sin| <= 1 it is within 2^-22 (|x1| + |x2|) of the exact value for the
+// double cos / sin (two roundings of cos / sin, one of the product, one of the
+// FMA), and the double expression is within 2^-51 (|x1| + |x2|) of it.  An
+// output whose f32 value lies farther than 2^-21 (|x1| + |x2|) from a bf16
+// rounding boundary therefore rounds like the double one; a pair with any
+// other output (about one in a thousand) is recomputed in double precision.
+__device__ __forceinline__ void rotate_chunk_f32(u32x4_t w1, u32x4_t w2, const double (*cs)[2],
+                                                 const float* cf, const float* sf, u32x4_t* out1,
+                                                 u32x4_t* out2) {
+  float x1[8], x2[8];
+  unpack8(w1, x1);
+  unpack8(w2, x2);
+  uint32_t y1[8], y2[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float a = x1[i], b = x2[i];
+    // the bound, kept clear of the subnormal range where errors are absolute
+    const float e = fmaxf((fabsf(a) + fabsf(b)) * 0x1p-21f, 0x1p-120f);
+    bool ok = true;
+    y1[i] = bf16_rne_checked(fmaf(a, cf[i], -(b * sf[i])), e, ok);
+    y2[i] = bf16_rne_checked(fmaf(b, cf[i], a * sf[i]), e, ok);
+    if (!ok) {  // per pair: a wave rarely has a lane here
+      const double ad = a, bd = b, c = cs[i][0], sn = cs[i][1];
+      y1[i] = bf16_rne(ad * c - bd * sn);
+      y2[i] = bf16_rne(bd * c + ad * sn);
+    }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
