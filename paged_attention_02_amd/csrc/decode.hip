@@ -12,14 +12,15 @@
 // (partition, kv head, tile of up to 16 grouped q heads, sequence), four
 // waves each.  A group of more than 16 q heads is served by several
 // work-groups that read the same K/V; they are placed on the same XCD (work
-// groups are handed to the 8 XCDs round-robin by linear id), so the repeat
-// read is an L2 hit rather than HBM traffic.  Each wave walks 32-token
+// groups are handed to the 8 XCDs round-robin by linear id), where the two
+// reads of a row mostly meet in L2.  Each wave walks 32-token
 // blocks (two pages) of the partition with its own online-softmax state; the
 // waves merge through LDS at the end.
 //
-// Per block a wave loads K and V rows with whole-cache-line loads (16 lanes
-// per 256-byte row; non-temporal when a single work-group reads each row),
-// into registers while the previous block is computed from LDS, then
+// Per block a wave loads K and V rows with whole-cache-line non-temporal loads
+// (16 lanes per 256-byte row; the hint keeps streamed rows from displacing
+// reusable lines, and after a large write a plain load of them is twice as
+// slow), into registers while the previous block is computed from LDS, then
 // stages them into its LDS slice (XOR-swizzled rows).  S^T = K Q^T
 // takes 8 v_mfma_f32_16x16x32_bf16 (tokens are M, the q heads N); each lane
 // then holds one head and 8 tokens, so the softmax max is an in-register
@@ -81,20 +82,12 @@ __device__ __forceinline__ int swz16(int row, int c) {
 __device__ __forceinline__ float xor16_max(float v) { return fmaxf(v, __shfl_xor(v, 16)); }
 __device__ __forceinline__ float xor16_sum(float v) { return v + __shfl_xor(v, 16); }
 
-template <bool NT>
-__device__ __forceinline__ u32x4_t ld_kv(const uint16_t* p) {
-  return NT ? ldg16_nt(p) : ldg16(p);
-}
-
 struct BlockLoad {
   u32x4_t k[8];
   u32x4_t v[8];
 };
 
-// NT: K/V loads carry the non-temporal hint.  Right when each row is read by
-// one work-group (up to 16 q heads per kv head); with more, the head tiles'
-// work-groups re-read the same rows and plain loads keep them in L2.
-template <int LAYOUT, bool NT>
+template <int LAYOUT>
 __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void paged_decode_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -192,13 +185,13 @@ void paged_decode_kernel(DecodeParams p) {
       const uint16_t* vb = vbase + pb * page_elems + lane_off;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        bl.k[s] = ld_kv<NT>(ka + 4 * s * row_stride);
-        bl.v[s] = ld_kv<NT>(va + 4 * s * row_stride);
+        bl.k[s] = ldg16_nt(ka + 4 * s * row_stride);
+        bl.v[s] = ldg16_nt(va + 4 * s * row_stride);
       }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        bl.k[4 + s] = ld_kv<NT>(kb + 4 * s * row_stride);
-        bl.v[4 + s] = ld_kv<NT>(vb + 4 * s * row_stride);
+        bl.k[4 + s] = ldg16_nt(kb + 4 * s * row_stride);
+        bl.v[4 + s] = ldg16_nt(vb + 4 * s * row_stride);
       }
     };
 
@@ -411,9 +404,8 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
                         (size_t)kNW * kHeadDim * kHT * sizeof(float);
   const size_t lds = stage > reduce ? stage : reduce;
   const int64_t groups = ((int64_t)(p.num_items + 7) / 8) * 8 * p.head_tiles;
-  void (*kernel)(DecodeParams) =
-      p.head_tiles == 1 ? paged_decode_kernel<LAYOUT, true> : paged_decode_kernel<LAYOUT, false>;
-  return launch_kernel(kernel, dim3((unsigned)groups), dim3(kNW * 64), lds, stream, p);
+  return launch_kernel(paged_decode_kernel<LAYOUT>, dim3((unsigned)groups), dim3(kNW * 64), lds,
+                       stream, p);
 }
 
 }  // namespace
