@@ -1,16 +1,20 @@
 """Standalone NeoX RoPE on the GPU vs the FP64 oracle, bit for bit.
 
-Both sides rotate in double precision from the bf16 inputs and round once to
-bf16, so the outputs must agree exactly: q and k together and each alone, in
-place, over positions 0 .. 32767, negative and extreme int32 positions, the
-Llama 3.1 frequency table, and the 32768-token long-prefill shape.  The
-standalone op must also give the same bits as the fused RoPE + append.
+Both sides give the double-precision rotation of the bf16 inputs rounded once
+to bf16 (the kernel forms it in f32 where that provably rounds the same and in
+double otherwise), so the outputs must agree exactly: q and k together and
+each alone, in place, over positions 0 .. 32767, negative and extreme int32
+positions, the Llama 3.1 frequency table, pairs built to cancel (which send
+many outputs down the double-precision path), and the 32768-token
+long-prefill shape.  The standalone op must also give the same bits as the
+fused RoPE + append.
 """
 import numpy as np
 import pytest
 import torch
 
 import workloads as W
+from oracle import bf16 as B
 from oracle import rope as R
 from tests.gpu_helpers import dev, host_bits, note
 from tests.lib_loader import ensure_built
@@ -48,6 +52,37 @@ def test_rope_neox_bit_exact(sides):
         assert np.array_equal(host_bits(qo), R.rope_neox_bf16(q, pos, 10000.0))
     if ko is not None:
         assert np.array_equal(host_bits(ko), R.rope_neox_bf16(k, pos, 10000.0))
+
+
+def test_rope_cancelling_pairs_bit_exact():
+    """x2 = bf16(x1 cot(angle)) for every pair, so x1 cos - x2 sin nearly
+    cancels: the rotated value is a small fraction of |x1| + |x2|, and many
+    outputs lie within the f32 form's error bound of a bf16 rounding
+    boundary (or below the size it needs), taking the double-precision path."""
+    nnz, hq, hkv = 256, 8, 2
+    rng = np.random.default_rng(4010)
+    pos = rng.integers(1, 32767, size=nnz, endpoint=True).astype(np.int32)
+    angle = pos[:, None].astype(np.float64) * R.inv_freq(10000.0, D)[None, :]   # [nnz, 64]
+    cot = np.cos(angle) / np.sin(angle)
+
+    def pairs(h):
+        x1 = B.to_f64(W.bf16_normal(rng, (nnz, h, D // 2)))
+        return B.from_f64(np.concatenate([x1, x1 * cot[:, None, :]], axis=-1))
+
+    q, k = pairs(hq), pairs(hkv)
+    # the inputs do cancel: the first half of the rotation is small against the inputs
+    x = B.to_f64(q)
+    y = R.rope_neox(x, pos[:, None], 10000.0)
+    ratio = np.abs(y[..., :D // 2]) / (np.abs(x[..., :D // 2]) + np.abs(x[..., D // 2:]))
+    assert np.median(ratio) < 2.0 ** -6
+    ensure_built()
+    qi, ki = dev(q), dev(k)
+    qo, ko = torch.empty_like(qi), torch.empty_like(ki)
+    note("rope_neox cancelling pairs")
+    assert oxa.oxa_rope_neox(qi, qo, ki, ko, dev(pos), rope_theta=10000.0) == oxa.OXA_OK
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(qo), R.rope_neox_bf16(q, pos, 10000.0))
+    assert np.array_equal(host_bits(ko), R.rope_neox_bf16(k, pos, 10000.0))
 
 
 def test_rope_in_place_equals_out_of_place():
