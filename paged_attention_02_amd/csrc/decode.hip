@@ -201,14 +201,25 @@ void paged_decode_kernel(DecodeParams p) {
       const int tb = tw + blk * 32;
       const bool okA = pids[2 * blk] >= 0;
       const bool okB = (tb + kPage < tw1) && pids[2 * blk + 1] >= 0;
-      const bool full = (tb + 32 <= tw1) && okA && okB;
+      const bool full = (tb + 32 <= tw1) && okA && okB;  // wave-uniform
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const int r = 4 * st + (lane >> 4);
-        const int off = swz16(r, lane & 15);
-        *reinterpret_cast<u32x4_t*>(ks + off) = bl.k[st];
-        const bool ok = full || ((tb + r < tw1) && (st < 4 ? okA : okB));
-        *reinterpret_cast<u32x4_t*>(vs + off) = ok ? bl.v[st] : u32x4_t{0, 0, 0, 0};
+      for (int st = 0; st < 8; ++st)
+        *reinterpret_cast<u32x4_t*>(ks + swz16(4 * st + (lane >> 4), lane & 15)) = bl.k[st];
+      if (full) {
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+          *reinterpret_cast<u32x4_t*>(vs + swz16(4 * st + (lane >> 4), lane & 15)) = bl.v[st];
+      } else {
+        // a bit mask, not a select: a select of the 16-byte rows is turned
+        // into a branch per row
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          const int r = 4 * st + (lane >> 4);
+          const uint32_t m = ((tb + r < tw1) && (st < 4 ? okA : okB)) ? 0xffffffffu : 0u;
+          const u32x4_t v = bl.v[st];
+          *reinterpret_cast<u32x4_t*>(vs + swz16(r, lane & 15)) =
+              u32x4_t{v[0] & m, v[1] & m, v[2] & m, v[3] & m};
+        }
       }
     };
 
