@@ -88,7 +88,8 @@ def test_single_sequence_mha_decode(layout, mode):
     assert_lse_close(got["lse"], lse, "mha lse")
 
 
-@pytest.mark.parametrize("hq,hkv", [(8, 2), (32, 8), (32, 1), (64, 1), (12, 4), (16, 16)])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (32, 8), (32, 1), (64, 1), (48, 1), (12, 4), (16, 16),
+                                    (1, 1)])
 @pytest.mark.parametrize("P", [1, 3])
 @pytest.mark.parametrize("mode", MODES)
 def test_grouped_decode_mixed_lengths(hq, hkv, P, mode):
