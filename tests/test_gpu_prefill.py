@@ -55,7 +55,8 @@ def run_paged(q_bits, qo_indptr, kp, vp, layout, indptr, ids, seq_lens, hkv, sca
     return dict(o=host_bits(o), lse=host(lse), status=host(status))
 
 
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 2), (32, 8), (32, 1), (12, 4)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (2, 1), (8, 2), (32, 8), (32, 1), (12, 4), (48, 2),
+                                    (64, 1), (512, 1)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_ragged_prefill_small(hq, hkv, causal):
     lens = [1, 17, 64, 130, 300]
