@@ -114,12 +114,29 @@ def check(code: int) -> None:
 
 
 # ------------------------------------------------------------------ marshalling
+#
+# These run on every call, so they avoid per-call imports and Python-level
+# stream objects: for a latency-bound launch the marshalling is a large part of
+# the host time.
+
+_torch = None
+_BF16_DTYPES = ()
+
+
+def _t():
+    """torch, imported on first use (the module loads without it)."""
+    global _torch, _BF16_DTYPES
+    if _torch is None:
+        import torch
+        _torch = torch
+        _BF16_DTYPES = (torch.bfloat16, torch.int16, torch.uint16)
+    return _torch
+
 
 def _ptr(t) -> Optional[int]:
     if t is None:
         return None
-    import torch
-    if not isinstance(t, torch.Tensor):
+    if not isinstance(t, _t().Tensor):
         raise TypeError("expected a torch tensor")
     if not t.is_cuda:
         raise ValueError("tensors must live on the GPU")
@@ -129,30 +146,29 @@ def _ptr(t) -> Optional[int]:
 
 
 def _bf16(t, name):
-    import torch
-    if t is not None and t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
-        raise TypeError(f"{name} must be bf16 (or its 16-bit bit pattern)")
+    if t is not None:
+        _t()
+        if t.dtype not in _BF16_DTYPES:
+            raise TypeError(f"{name} must be bf16 (or its 16-bit bit pattern)")
     return _ptr(t)
 
 
 def _i32(t, name):
-    import torch
-    if t is not None and t.dtype != torch.int32:
+    if t is not None and t.dtype != _t().int32:
         raise TypeError(f"{name} must be int32")
     return _ptr(t)
 
 
 def _f32(t, name):
-    import torch
-    if t is not None and t.dtype != torch.float32:
+    if t is not None and t.dtype != _t().float32:
         raise TypeError(f"{name} must be float32")
     return _ptr(t)
 
 
 def _state_dtype(t, name) -> int:
     """oxa_dtype of an attention-state tensor: bf16 (or its bits) or float32."""
-    import torch
-    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+    torch = _t()
+    if t.dtype in _BF16_DTYPES:
         return OXA_DTYPE_BF16
     if t.dtype == torch.float32:
         return OXA_DTYPE_F32
@@ -160,7 +176,8 @@ def _state_dtype(t, name) -> int:
 
 
 def _shape(t, shape, name):
-    if t is not None and tuple(t.shape) != tuple(shape):
+    # torch.Size is a tuple: it compares with a tuple as it is
+    if t is not None and t.shape != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
@@ -180,16 +197,23 @@ def _pools(k_pages, v_pages, lay, hkv=None):
 
 
 def _no_alloc_under_capture(what):
-    import torch
-    if torch.cuda.is_current_stream_capturing():
+    if _t().cuda.is_current_stream_capturing():
         raise RuntimeError(f"{what}: pass `workspace` when capturing a graph "
                            "(the binding would otherwise allocate one inside the capture)")
 
 
 def _stream(stream) -> int:
-    import torch
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+    """The raw HIP stream: `stream`'s, else the current stream of the current
+    device (read without building a torch Stream object, which costs more than
+    a small kernel launch; the public call where that entry is missing)."""
+    torch = _t()
+    if stream is not None:
+        return stream.cuda_stream
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    dev = getattr(torch._C, "_cuda_getDevice", None)
+    if raw is not None and dev is not None:
+        return raw(dev())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _layout(layout) -> int:
