@@ -13,9 +13,10 @@
 // The merge reads every state once and does a few flops per byte: it is
 // bound by HBM bandwidth (or, when small, by load latency).  Lanes own 16-byte
 // pieces of the 128-wide rows (16 lanes per bf16 row, 32 per f32 row), so each
-// wave reads whole rows with 16-byte loads.  A lane issues the loads of eight
-// states together, then folds them into a running (max, sum, accumulator) in
-// base 2.  States are addressed through element strides, which covers both the
+// wave reads whole rows with 16-byte loads.  A lane issues the loads of a
+// batch of states together - sixteen when a unit merges more than eight (the
+// split-K decode's partitions: one memory round trip instead of two), else
+// eight - then folds them into a running (max, sum, accumulator) in base 2.  States are addressed through element strides, which covers both the
 // operator's [row][state][head][128] layout and the split-K decode workspace
 // [sequence][head][partition][128].
 #include "device_common.h"
@@ -25,7 +26,6 @@ namespace oxa {
 namespace {
 
 constexpr int kThreads = 128;
-constexpr int kBatch = 8;  // states whose loads are in flight together
 
 template <bool F32>
 __device__ __forceinline__ void unpack(u32x4_t w, float* x) {
@@ -41,7 +41,8 @@ __device__ __forceinline__ void unpack(u32x4_t w, float* x) {
   }
 }
 
-template <bool IN_F32, bool OUT_F32, bool PAIR>
+// KB: states whose loads are in flight together
+template <bool IN_F32, bool OUT_F32, bool PAIR, int KB>
 __global__ __launch_bounds__(kThreads) void merge_states_kernel(MergeLaunch p) {
   constexpr int kEsz = IN_F32 ? 4 : 2;    // bytes per input element
   constexpr int kEpl = 16 / kEsz;         // elements per lane
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void merge_states_kernel(MergeLaunch p) {
   const unsigned char* v0 = static_cast<const unsigned char*>(p.v[0]);
   const unsigned char* v1 = static_cast<const unsigned char*>(p.v[1]);
 
-  constexpr int kB = PAIR ? 2 : kBatch;
+  constexpr int kB = PAIR ? 2 : KB;
   float m = -INFINITY, wsum = 0.f, acc[kEpl];
 #pragma unroll
   for (int e = 0; e < kEpl; ++e) acc[e] = 0.f;
@@ -85,11 +86,18 @@ __global__ __launch_bounds__(kThreads) void merge_states_kernel(MergeLaunch p) {
       l[j] = in ? lv * kLog2e : -INFINITY;
       w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vp));
     }
+    // every load of the batch is issued before any is used: one memory round
+    // trip per batch (the compiler otherwise waits for the lse values first
+    // and streams the rows in a few at a time)
+    __builtin_amdgcn_sched_group_barrier(0x020, 2 * kB, 0);
+    __builtin_amdgcn_sched_barrier(0);
     float cm = m;
 #pragma unroll
     for (int j = 0; j < kB; ++j) cm = fmaxf(cm, l[j]);
-    if (cm == -INFINITY) continue;  // nothing live yet
-    const float r = fast_exp2(m - cm);  // 0 while m is still -inf
+    // no branch on "nothing live yet": with every lse so far -inf, the
+    // reference is 0, every weight exp2(-inf) = 0, and the state stays empty
+    const float cref = cm == -INFINITY ? 0.f : cm;
+    const float r = fast_exp2(m - cref);  // 0 while m is still -inf
     wsum *= r;
 #pragma unroll
     for (int e = 0; e < kEpl; ++e) acc[e] *= r;
@@ -97,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void merge_states_kernel(MergeLaunch p) {
     for (int j = 0; j < kB; ++j) {
       float x[kEpl];
       unpack<IN_F32>(w[j], x);
-      const float wt = fast_exp2(l[j] - cm);  // 0 for an empty state
+      const float wt = fast_exp2(l[j] - cref);  // 0 for an empty state
       const bool live = l[j] != -INFINITY;
       wsum += wt;
 #pragma unroll
@@ -137,8 +145,9 @@ template <bool IN_F32, bool OUT_F32>
 hipError_t launch_t(const MergeLaunch& a, hipStream_t stream) {
   constexpr int kUpb = kThreads / (kHeadDim / (16 / (IN_F32 ? 4 : 2)));
   const int64_t groups = (a.units + kUpb - 1) / kUpb;
-  void (*kernel)(MergeLaunch) = a.pair ? merge_states_kernel<IN_F32, OUT_F32, true>
-                                       : merge_states_kernel<IN_F32, OUT_F32, false>;
+  void (*kernel)(MergeLaunch) = a.pair         ? merge_states_kernel<IN_F32, OUT_F32, true, 2>
+                                : a.states > 8 ? merge_states_kernel<IN_F32, OUT_F32, false, 16>
+                                               : merge_states_kernel<IN_F32, OUT_F32, false, 8>;
   return launch_kernel(kernel, dim3((unsigned)groups), dim3(kThreads), 0, stream, a);
 }
 
