@@ -121,8 +121,8 @@ def test_grouped_decode_mixed_lengths(hq, hkv, P, mode):
 @pytest.mark.parametrize("P", [1, 2])
 @pytest.mark.parametrize("mode", MODES)
 def test_decode_several_head_tiles_per_kv_head(layout, P, mode):
-    """24 q heads per kv head: two work-groups (16 + 8 heads) read the same K/V
-    rows, the kernel form with plain (not non-temporal) loads, in both layouts."""
+    """24 q heads per kv head: two work-groups (16 + 8 heads, the second tile
+    partly empty) read the same K/V rows, in both layouts."""
     lens = [5, 160, 1000, 47]
     case = W.decode_case(90 + P, batch=len(lens), num_qo_heads=48, num_kv_heads=2, seq_lens=lens,
                          num_pages=sum(-(-n // 16) for n in lens) + 4, layout=layout,
