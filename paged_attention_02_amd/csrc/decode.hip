@@ -79,8 +79,6 @@ __device__ __forceinline__ int swz16(int row, int c) {
   return row * 256 + ((c ^ sw) << 4);
 }
 
-__device__ __forceinline__ float xor16_max(float v) { return fmaxf(v, __shfl_xor(v, 16)); }
-__device__ __forceinline__ float xor16_sum(float v) { return v + __shfl_xor(v, 16); }
 
 struct BlockLoad {
   u32x4_t k[8];
@@ -261,7 +259,7 @@ void paged_decode_kernel(DecodeParams p) {
       }
       // a block with no visible key keeps max -inf (also for a zero scale,
       // where -inf * 0 would be NaN)
-      const float mred = pair_max32(xor16_max(mraw));
+      const float mred = pair_max32(pair_max16(mraw));
       const float mblk = mred == -INFINITY ? -INFINITY : mred * p.scale_log2;
       // Lazy rescaling: exponentials are taken against a reference max that
       // only moves when a score exceeds it by more than 2^8, so probabilities
@@ -323,7 +321,7 @@ void paged_decode_kernel(DecodeParams p) {
   }
 
   // ---- merge the waves' states through LDS -------------------------------
-  lsum = pair_sum32(xor16_sum(lsum));
+  lsum = pair_sum32(pair_sum16(lsum));
   __syncthreads();  // staging area is reused below
   float* red_m = reinterpret_cast<float*>(smem);  // [kNW][16]
   float* red_l = red_m + kNW * kHT;               // [kNW][16]
