@@ -50,25 +50,6 @@ struct AppendParams {
   double inv_freq[64];
 };
 
-// Check one token: 0 if it may be written, else its status code.  Also returns
-// the target page (valid only when the code is 0).
-__device__ __forceinline__ int check_token(const AppendParams& p, int t, int* page_out) {
-  const int b = p.batch_indices[t];
-  if (b < 0 || b >= p.batch) return kStatusBatchIndex;
-  const int lo = p.page_indptr[b];
-  const int hi = p.page_indptr[b + 1];
-  const int pos = p.positions[t];
-  // an indptr that leaves the page-index array gives the sequence no capacity
-  const bool ptr_ok = lo >= 0 && hi >= lo && hi <= p.num_page_entries;
-  const int64_t cap = ptr_ok ? (int64_t)(hi - lo) * kPage : 0;
-  if (pos < 0 || (int64_t)pos >= cap) return kStatusCapacity;
-  const int page = p.page_indices[lo + pos / kPage];
-  if (page < 0 || page >= p.num_pages) return kStatusPageRange;
-  if (p.page_refcounts[page] != 1) return kStatusNotExclusive;
-  *page_out = page;
-  return 0;
-}
-
 constexpr int kNone = 0x7fffffff;        // "no failing token"
 constexpr int kCheckPer = 4;             // tokens per thread per pass
 constexpr int kCheckTile = 256 * kCheckPer;
@@ -180,9 +161,15 @@ __global__ __launch_bounds__(256) void append_rope_kernel(AppendParams p) {
   const int hsub = lane >> 3;  // 0..7
   const int nwaves = gridDim.x * 4;
   for (int t = blockIdx.x * 4 + wave; t < p.nnz; t += nwaves) {
-    int page;
-    if (check_token(p, t, &page) != 0) continue;  // cannot happen after the check
+    // Every token passed the check pass (the gate above), so only its page is
+    // looked up here, without branches: the index chain (batch index, indptr,
+    // page id) is issued first and waited for only where K and V are stored,
+    // after the sin/cos and the q rotation.  The clamps keep every access in
+    // bounds whatever the tables hold.
     const int pos = p.positions[t];
+    const int b = min(max(p.batch_indices[t], 0), p.batch - 1);
+    const int e = min(max(p.page_indptr[b] + (pos >> 4), 0), p.num_page_entries - 1);
+    const int page = min(max(p.page_indices[e], 0), p.num_pages - 1);
     const int slot = pos & (kPage - 1);
     const uint16_t* ki = p.k_in + (int64_t)t * p.hkv * kHeadDim;
     const uint16_t* vi = p.v_in + (int64_t)t * p.hkv * kHeadDim;
