@@ -165,7 +165,8 @@ __global__ __launch_bounds__(256) void append_rope_kernel(AppendParams p) {
     // looked up here, without branches: the index chain (batch index, indptr,
     // page id) is issued first and waited for only where K and V are stored,
     // after the sin/cos and the q rotation.  The clamps keep every access in
-    // bounds whatever the tables hold.
+    // bounds whatever the tables hold (a call that reaches this loop has at
+    // least one page entry: with none, every token fails the check).
     const int pos = p.positions[t];
     const int b = min(max(p.batch_indices[t], 0), p.batch - 1);
     const int e = min(max(p.page_indptr[b] + (pos >> 4), 0), p.num_page_entries - 1);
