@@ -173,10 +173,15 @@ void paged_decode_kernel(DecodeParams p) {
     // (straight-line code keeps the wait counters exact): a missing or invalid
     // page reads page 0 and those rows are discarded; a block past the
     // window's end re-reads its last block (a cache hit, never used).
-    auto issue = [&](int blk, BlockLoad& bl) {
+    // The page-id pair of block blk (pair of a block past the window's end:
+    // its last block's).
+    auto pair_of = [&](int blk) {
       const int bi = min(blk, nb - 1);
-      const int pa = max(pids[2 * bi], 0);
-      const int pb = max(pids[2 * bi + 1], 0);
+      return int2{max(pids[2 * bi], 0), max(pids[2 * bi + 1], 0)};
+    };
+    auto issue = [&](int2 pp, BlockLoad& bl) {
+      const int pa = __builtin_amdgcn_readfirstlane(pp.x);
+      const int pb = __builtin_amdgcn_readfirstlane(pp.y);
       const uint16_t* ka = kbase + pa * page_elems + lane_off;
       const uint16_t* kb = kbase + pb * page_elems + lane_off;
       const uint16_t* va = vbase + pa * page_elems + lane_off;
@@ -305,15 +310,21 @@ void paged_decode_kernel(DecodeParams p) {
 
     // One register set holds the next block's loads while the current one is
     // computed from LDS; the loaded block is staged at the end of the step.
+    // The page ids of the next issue are read a step ahead, before this
+    // step's LDS writes, so the loads go out as soon as the staged block is
+    // written instead of after an LDS read queued behind those writes.
     BlockLoad bl;
     int blk = wave;
+    int2 pp = pair_of(blk);
     if (blk < nb) {
-      issue(blk, bl);
+      issue(pp, bl);
+      pp = pair_of(blk + kNW);
       stage(blk, bl);
     }
     while (blk < nb) {
       const int nxt = blk + kNW;
-      issue(nxt, bl);
+      issue(pp, bl);
+      pp = pair_of(nxt + kNW);
       compute(blk);
       if (nxt < nb) stage(nxt, bl);
       blk = nxt;
