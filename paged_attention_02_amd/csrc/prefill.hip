@@ -458,10 +458,9 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
 
     const int key0 = kt * kBN;
     const bool need_mask = (key0 + kBN > si.klen) || (p.causal && key0 + kBN - 1 > wg_min_lim);
-    // S^T[key][col] of the paged kernel for keys 32*mb .. +31: 8 k-steps over
-    // the 128 dims, all 8 K fragments read before the MFMAs (scheduling
-    // groups): the paged kernel measured faster this way, the ragged one does not
-    auto paged_scores = [&](int mb) {
+    // S^T[key][col] for keys 32*mb .. +31: 8 k-steps over the 128 dims, all
+    // 8 K fragments read before the MFMAs (scheduling groups)
+    auto scores = [&](int mb) {
       f32x16_t s = f32x16_t{};
       u32x4_t kf[8];
 #pragma unroll
@@ -473,20 +472,11 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // then MFMAs
       return s;
     };
-    f32x16_t s_carry = f32x16_t{};  // paged: the second half's scores
+    f32x16_t s_carry = f32x16_t{};  // the second half's scores
     // Two online-softmax steps of 32 keys per tile (keeps half the scores live).
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      // S^T[key][col] for keys 32*mb .. +31: 8 k-steps over the 128 dims
-      f32x16_t s = f32x16_t{};
-      if constexpr (PAGED) {
-        s = mb == 0 ? paged_scores(0) : s_carry;
-      } else {
-#pragma unroll
-        for (int st = 0; st < 8; ++st)
-          s = mfma_32x32x16(*reinterpret_cast<const u32x4_t*>(ks + mb * 8192 + koff[st]), qf[st],
-                            s);
-      }
+      f32x16_t s = mb == 0 ? scores(0) : s_carry;
       // V^T fragments of this half, read now so that their LDS latency passes
       // under the softmax (they do not depend on it).  Transpose read: lanes
       // 4e..4e+3 of a 16-lane group address row (32*mb + 16*h + 4*(l/32) + e)
@@ -564,14 +554,11 @@ __global__ __launch_bounds__(kNW * 64) void prefill_kernel(PrefillParams p) {
           probs(BufTag<0>{});
       }
       lsum += psum;
-      if constexpr (PAGED) {
-        // the second half's S MFMAs go ahead of this half's P.V MFMAs, so its
-        // softmax can start while they still occupy the matrix core (1 % on
-        // the long paged prefill; the ragged kernel measured slower this way)
-        if (mb == 0) {
-          s_carry = paged_scores(1);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      // The second half's S MFMAs go ahead of this half's P.V MFMAs, so its
+      // softmax can start while they still occupy the matrix core.
+      if (mb == 0) {
+        s_carry = scores(1);
+        __builtin_amdgcn_sched_barrier(0);
       }
       // O^T += V^T * P^T over the 2 k-steps of 16 keys in this block.
 #pragma unroll
