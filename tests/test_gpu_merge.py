@@ -46,7 +46,7 @@ def _check(got_t, ref, dtype, what):
 
 @pytest.mark.parametrize("din,dout", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "bf16"),
                                       ("f32", "f32")])
-@pytest.mark.parametrize("R,S,H", [(37, 5, 6), (9, 19, 3), (1, 1, 1), (3, 8, 32)])
+@pytest.mark.parametrize("R,S,H", [(37, 5, 6), (9, 19, 3), (1, 1, 1), (3, 8, 32), (4, 12, 5), (2, 40, 7)])
 def test_merge_states_vs_oracle(din, dout, R, S, H):
     case = W.merge_case(2000 + R + S + H, R, S, H, dtype=din)
     ensure_built()
